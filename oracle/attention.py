@@ -1,0 +1,274 @@
+"""Plain float64 definitions of what the attention library computes.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): slow, obviously correct,
+materialises the full score matrix S and probability matrix P. Inputs may be
+torch CPU tensors (float32 / bfloat16) or numpy arrays; every stored value is
+upcast exactly to float64 before any arithmetic, so input quantisation is not
+counted as error.
+
+Readings taken where the pages leave a step open (each one is listed with its
+reason in the design notes of the repository):
+  * scale: S = scale * Q K^T with ``scale`` an explicit argument ([P2] §一 gives
+    1/sqrt(d_k); the [P1] §2.2 pseudocode omits it).
+  * causal alignment when the query count Lq is below the key count Lk:
+    bottom-right, i.e. query t sits at absolute position Lk - Lq + t and sees
+    keys 0 .. Lk - Lq + t. This is what "verify prefix + K drafts in one
+    forward" ([P3], speculative-sampling item) needs; with Lq == Lk it is the
+    usual lower triangle.
+  * a row that sees no key has output 0 and log-sum-exp -inf.
+  * log-sum-exp uses the natural logarithm.
+"""
+
+import numpy as np
+
+try:  # torch is only used to read bfloat16 tensors exactly
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+
+def _f64(x):
+    """Exact float64 copy of a torch tensor or array-like."""
+    if torch is not None and isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _i64(x):
+    if torch is not None and isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.int64).numpy()
+    return np.asarray(x, dtype=np.int64)
+
+
+def causal_visibility(lq, lk):
+    """Boolean [lq, lk]: True where query t may attend key j.
+
+    Bottom-right alignment: key j is visible to query t iff j <= (lk - lq) + t.
+    """
+    t = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    return j <= (lk - lq) + t
+
+
+def masked_attention(q, k, v, scale, visible, return_p=False):
+    """softmax(scale * q k^T restricted to ``visible``) v, in float64.
+
+    Standard attention as [P1] §2.1 and [P2] §一 define it: the whole score
+    matrix S is formed, the softmax is taken row by row over the visible keys
+    (subtracting the row maximum first, which leaves the softmax unchanged),
+    and the normalised P multiplies V.
+
+    q [Lq, D], k [Lk, D], v [Lk, Dv]; ``visible`` bool [Lq, Lk] or None (all).
+    Returns (o [Lq, Dv], lse [Lq]) and, if ``return_p``, also P [Lq, Lk].
+    Rows with no visible key give o = 0, lse = -inf, P = 0.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lq, lk = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    if visible is None:
+        visible = np.ones((lq, lk), dtype=bool)
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1) if lk > 0 else np.full(lq, -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    p = np.where(visible, np.exp(s - m_safe[:, None]), 0.0)
+    l = p.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    p = p / l_safe[:, None]
+    o = p @ v
+    lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    if return_p:
+        return o, lse, p
+    return o, lse
+
+
+def dense_attention(q, k, v, scale, causal, return_p=False):
+    """One (batch, head) of exact attention, causal mask bottom-right aligned."""
+    lq, lk = np.shape(q)[0], np.shape(k)[0]
+    vis = causal_visibility(lq, lk) if causal else None
+    return masked_attention(q, k, v, scale, vis, return_p=return_p)
+
+
+def prefill(q, k, v, scale, causal, heads=None):
+    """Exact attention over [B, H, L, D] tensors, one (b, h) at a time.
+
+    Returns (o [B, H, Lq, D] float64, lse [B, H, Lq] float64). ``heads`` may be
+    an iterable of (b, h) pairs to evaluate only those (other entries are NaN),
+    for sampled checks at full size.
+    """
+    B, H, lq, D = q.shape
+    o = np.full((B, H, lq, v.shape[3]), np.nan)
+    lse = np.full((B, H, lq), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        o[b, h], lse[b, h] = dense_attention(q[b, h], k[b, h], v[b, h], scale, causal)
+    return o, lse
+
+
+def online_softmax_attention(q, k, v, scale, causal, bm, bn):
+    """Tiled attention with the online-softmax recurrence, in float64.
+
+    Follows the FlashAttention tiling of [P1] §2.2: Q is cut into row blocks of
+    ``bm`` rows (outer loop, as FlashAttention-2 orders it in [P3]) and K, V into
+    blocks of ``bn`` keys (inner loop). Each row keeps a running maximum m, a
+    running exponential sum l and an unnormalised output O. For each key block:
+    the block's scores are formed, the new maximum is the larger of the old one
+    and the block's row maximum, the old l and O are scaled by exp(m_old - m_new),
+    the block's exp(S - m_new) is added to l and its product with V_j to O. The
+    division by l happens once per row block, after its last key block.
+
+    Starting state m = -inf, l = 0, O = 0. A factor exp(m_old - m_new) with
+    m_old = -inf is 0; -inf - (-inf) is never evaluated (a fully masked block
+    leaves the state untouched). Returns (o [Lq, Dv], lse [Lq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lq, lk = q.shape[0], k.shape[0]
+    vis_all = causal_visibility(lq, lk) if causal else np.ones((lq, lk), dtype=bool)
+    out = np.zeros((lq, v.shape[1]))
+    lse = np.full(lq, -np.inf)
+    for r0 in range(0, lq, bm):
+        r1 = min(r0 + bm, lq)
+        m = np.full(r1 - r0, -np.inf)
+        l = np.zeros(r1 - r0)
+        acc = np.zeros((r1 - r0, v.shape[1]))
+        for c0 in range(0, lk, bn):
+            c1 = min(c0 + bn, lk)
+            vis = vis_all[r0:r1, c0:c1]
+            s = scale * (q[r0:r1] @ k[c0:c1].T)
+            s = np.where(vis, s, -np.inf)
+            m_new = np.maximum(m, s.max(axis=1))
+            live = np.isfinite(m_new)
+            m_ref = np.where(live, m_new, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
+            p = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
+            l = alpha * l + p.sum(axis=1)
+            acc = alpha[:, None] * acc + p @ v[c0:c1]
+            m = m_new
+        done = l > 0
+        out[r0:r1] = np.where(done[:, None], acc / np.where(done, l, 1.0)[:, None], 0.0)
+        lse[r0:r1] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)
+    return out, lse
+
+
+def paged_gather(pool, block_tables, seq_lens, block_size=16):
+    """Read each sequence's cache rows back through its block table.
+
+    PagedAttention as [P1] §3.2, [P3] and [P4] describe it: the cache is a pool
+    of fixed-size physical blocks (16 tokens), and each sequence owns a table
+    mapping its logical block n to a physical block id. Token t of sequence b
+    lives in logical block t // block_size, slot t % block_size, i.e. at
+    pool[block_tables[b][t // block_size], :, t % block_size, :].
+
+    pool [num_blocks, H, block_size, D] (any dtype); returns a list with one
+    array per sequence, [H, seq_len_b, D], holding exactly the pool's values
+    (same dtype, no arithmetic). Table entries past the last used block and
+    slots past seq_len are never read.
+    """
+    tables = _i64(block_tables)
+    lens = _i64(seq_lens)
+    is_torch = torch is not None and isinstance(pool, torch.Tensor)
+    out = []
+    for b in range(tables.shape[0]):
+        n = int(lens[b])
+        tok = np.arange(n)
+        phys = tables[b][tok // block_size]
+        slot = tok % block_size
+        if is_torch:
+            rows = pool[torch.from_numpy(phys), :, torch.from_numpy(slot), :]  # [n, H, D]
+            out.append(rows.permute(1, 0, 2).contiguous())
+        else:
+            rows = np.asarray(pool)[phys, :, slot, :]
+            out.append(np.ascontiguousarray(np.transpose(rows, (1, 0, 2))))
+    return out
+
+
+def paged_attention(q, k_pool, v_pool, block_tables, seq_lens, scale, causal,
+                    block_size=16, heads=None):
+    """Attention of q [B, H, Lq, D] over each sequence's paged K/V.
+
+    The key count of sequence b is seq_lens[b] and includes the Lq new tokens,
+    so with ``causal`` query t sits at position seq_len - Lq + t (bottom-right).
+    Returns (o [B, H, Lq, D], lse [B, H, Lq]) in float64; with ``heads`` only
+    those (b, h) pairs are evaluated (others NaN).
+    """
+    B, H, lq, D = q.shape
+    o = np.full((B, H, lq, v_pool.shape[3]), np.nan)
+    lse = np.full((B, H, lq), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    bsel = sorted({b for b, _ in pairs})
+    tables = _i64(block_tables)
+    lens = _i64(seq_lens)
+    for b in bsel:
+        kc = paged_gather(k_pool, tables[b:b + 1], lens[b:b + 1], block_size)[0]
+        vc = paged_gather(v_pool, tables[b:b + 1], lens[b:b + 1], block_size)[0]
+        for bb, h in pairs:
+            if bb != b:
+                continue
+            o[b, h], lse[b, h] = dense_attention(q[b, h], kc[h], vc[h], scale, causal)
+    return o, lse
+
+
+def split_ranges(seq_len, num_splits, block_size=16):
+    """Token ranges of the split-KV partition of one sequence.
+
+    FlashDecoding ([P3]) cuts the key range along the sequence into pieces
+    handled independently. Reading used here: the sequence's nb = ceil(seq_len
+    / block_size) blocks are cut into ``num_splits`` contiguous, block-aligned
+    ranges of ceil(nb / num_splits) blocks; the last ranges may be short or
+    empty. Returns a list of (start, end) token indices.
+    """
+    nb = -(-seq_len // block_size)
+    per = -(-nb // num_splits) if nb > 0 else 0
+    out = []
+    for p in range(num_splits):
+        b0 = min(p * per, nb)
+        b1 = min((p + 1) * per, nb)
+        out.append((min(b0 * block_size, seq_len), min(b1 * block_size, seq_len)))
+    return out
+
+
+def split_partials(q, k, v, scale, causal, num_splits, block_size=16):
+    """Per-split normalised outputs and log-sum-exps for one (batch, head).
+
+    q [Lq, D], k/v [Lk, D] (the whole key range of the sequence). Split p
+    attends only keys in its range (with the same absolute causal mask as the
+    unsplit problem) and returns its own softmax-normalised o_p and lse_p; an
+    empty or fully masked range gives o_p = 0, lse_p = -inf.
+    Returns (o_parts [S, Lq, Dv], lse_parts [S, Lq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lq, lk = q.shape[0], k.shape[0]
+    vis = causal_visibility(lq, lk) if causal else np.ones((lq, lk), dtype=bool)
+    o_parts = np.zeros((num_splits, lq, v.shape[1]))
+    lse_parts = np.full((num_splits, lq), -np.inf)
+    for p, (a, b) in enumerate(split_ranges(lk, num_splits, block_size)):
+        if b > a:
+            o_parts[p], lse_parts[p] = masked_attention(q, k[a:b], v[a:b], scale, vis[:, a:b])
+    return o_parts, lse_parts
+
+
+def lse_merge(o_parts, lse_parts):
+    """Combine split-KV partials into the full result.
+
+    Each partial p holds softmax-normalised o_p and lse_p = log(sum of exp of
+    its scores). The full softmax is recovered by weighting o_p with
+    exp(lse_p - M) for M = max_p lse_p and dividing by the sum of the weights;
+    the full lse is M + log(sum of weights). This is the same rescaling that
+    merges two key blocks in the online-softmax recurrence of [P1] §2.2, done
+    once across splits -- the cross-block reduction FlashDecoding ([P3])
+    describes. Rows whose partials are all -inf give o = 0, lse = -inf.
+
+    o_parts [S, ..., D], lse_parts [S, ...] -> (o [..., D], lse [...]).
+    """
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    m = lse_parts.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m_safe[None]), 0.0)
+    wsum = w.sum(axis=0)
+    wsum_safe = np.where(empty, 1.0, wsum)
+    o = (w[..., None] * o_parts).sum(axis=0) / wsum_safe[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, -np.inf, m_safe + np.log(wsum_safe))
+    return o, lse

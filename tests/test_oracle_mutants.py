@@ -1,0 +1,219 @@
+"""The oracle's pins are sharp enough to catch plausible mistakes.
+
+Each mutant below is a copy of one oracle function with one planted mistake
+(a dropped term, a wrong sign or index, a transposed operand, a misplaced
+step). Every mutant must fail at least one of the pin checks that the real
+oracle passes. Mistakes are planted here, on the CPU, in copies; the oracle
+itself is untouched.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.test_oracle_pins import (
+    ALL_CHECKS,
+    check_gather_contiguous,
+    check_merge_closed_forms,
+    check_paging_fixture,
+    check_split_merge,
+)
+
+
+def _attn_variant(q, k, v, scale, causal, bug):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    lq, lk = q.shape[0], k.shape[0]
+    s = (q @ k.T) if bug == "no_scale" else scale * (q @ k.T)
+    t = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    if bug == "strict_causal":
+        vis = j < (lk - lq) + t
+    elif bug == "top_left_causal":
+        vis = j <= t
+    elif bug == "off_by_one_causal":
+        vis = j <= (lk - lq) + t + 1
+    else:
+        vis = j <= (lk - lq) + t
+    if not causal:
+        vis = np.ones((lq, lk), dtype=bool)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    empty = ~np.isfinite(m)
+    ms = np.where(empty, 0.0, m)
+    if bug == "exp_sign":
+        p = np.where(vis, np.exp(ms[:, None] - s), 0.0)
+    else:
+        p = np.where(vis, np.exp(s - ms[:, None]), 0.0)
+    l = p.sum(axis=1)
+    ls = np.where(empty, 1.0, l)
+    if bug != "no_normalise":
+        p = p / ls[:, None]
+    o = (p @ k) if bug == "k_for_v" else (p @ v)
+    if bug == "lse_no_log":
+        lse = np.where(empty, -np.inf, ms + ls)
+    elif bug == "lse_log2":
+        lse = np.where(empty, -np.inf, ms + np.log2(ls))
+    elif bug == "lse_no_max":
+        lse = np.where(empty, -np.inf, np.log(ls))
+    else:
+        lse = np.where(empty, -np.inf, ms + np.log(ls))
+    return o, lse
+
+
+DENSE_BUGS = ["no_scale", "strict_causal", "top_left_causal", "off_by_one_causal", "exp_sign",
+              "no_normalise", "k_for_v", "lse_no_log", "lse_log2", "lse_no_max"]
+
+
+def _fails_some(checks, fn):
+    for c in checks:
+        try:
+            c(fn)
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("bug", DENSE_BUGS)
+def test_dense_mutant_caught(bug):
+    # the unmutated copy passes, the mutant does not
+    assert not _fails_some(ALL_CHECKS, lambda q, k, v, s, c: _attn_variant(q, k, v, s, c, None))
+    assert _fails_some(ALL_CHECKS, lambda q, k, v, s, c: _attn_variant(q, k, v, s, c, bug))
+
+
+def _online_variant(q, k, v, scale, causal, bm, bn, bug):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    lq, lk = q.shape[0], k.shape[0]
+    vis_all = (np.arange(lk)[None, :] <= (lk - lq) + np.arange(lq)[:, None]) if causal \
+        else np.ones((lq, lk), dtype=bool)
+    out = np.zeros((lq, v.shape[1]))
+    lse = np.full(lq, -np.inf)
+    for r0 in range(0, lq, bm):
+        r1 = min(r0 + bm, lq)
+        m = np.full(r1 - r0, -np.inf)
+        l = np.zeros(r1 - r0)
+        acc = np.zeros((r1 - r0, v.shape[1]))
+        for c0 in range(0, lk, bn):
+            c1 = min(c0 + bn, lk)
+            vis = vis_all[r0:r1, c0:c1]
+            s = np.where(vis, scale * (q[r0:r1] @ k[c0:c1].T), -np.inf)
+            m_new = np.maximum(m, s.max(axis=1))
+            m_ref = np.where(np.isfinite(m_new), m_new, 0.0)
+            if bug == "alpha_sign":
+                alpha = np.where(np.isfinite(m), np.exp(m_ref - m), 0.0)
+            else:
+                alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
+            p = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
+            l = (l if bug == "no_rescale_l" else alpha * l) + p.sum(axis=1)
+            acc = (acc if bug == "no_rescale_o" else alpha[:, None] * acc) + p @ v[c0:c1]
+            m = m_new
+            if bug == "normalise_each_tile":
+                acc = acc / np.where(l > 0, l, 1.0)[:, None]
+        done = l > 0
+        if bug == "normalise_each_tile":
+            out[r0:r1] = acc
+        else:
+            out[r0:r1] = np.where(done[:, None], acc / np.where(done, l, 1.0)[:, None], 0.0)
+        lse[r0:r1] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)
+    return out, lse
+
+
+@pytest.mark.parametrize("bug", ["alpha_sign", "no_rescale_l", "no_rescale_o", "normalise_each_tile"])
+def test_online_mutant_caught(bug):
+    fn = lambda q, k, v, s, c: _online_variant(q, k, v, s, c, 2, 3, None)  # noqa: E731
+    assert not _fails_some(ALL_CHECKS, fn)
+    mut = lambda q, k, v, s, c: _online_variant(q, k, v, s, c, 2, 3, bug)  # noqa: E731
+    assert _fails_some(ALL_CHECKS, mut)
+
+
+def _gather_variant(pool, block_tables, seq_lens, block_size=16, bug=None):
+    import torch
+    tables = np.asarray(block_tables.tolist() if hasattr(block_tables, "tolist") else block_tables)
+    lens = [int(x) for x in (seq_lens.tolist() if hasattr(seq_lens, "tolist") else seq_lens)]
+    out = []
+    for b in range(tables.shape[0]):
+        n = lens[b]
+        tok = np.arange(n)
+        if bug == "logical_not_physical":
+            phys = tok // block_size
+        elif bug == "slot_block_swapped":
+            phys = tables[b][tok % tables.shape[1]]
+        elif bug == "next_block":
+            phys = tables[b][np.minimum(tok // block_size + 1, tables.shape[1] - 1)]
+        else:
+            phys = tables[b][tok // block_size]
+        slot = (tok // block_size) % block_size if bug == "slot_block_swapped" else tok % block_size
+        if isinstance(pool, torch.Tensor):
+            rows = pool[torch.from_numpy(phys), :, torch.from_numpy(slot), :]
+            out.append(rows.permute(1, 0, 2).contiguous())
+        else:
+            out.append(np.ascontiguousarray(np.transpose(np.asarray(pool)[phys, :, slot, :], (1, 0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("bug", ["logical_not_physical", "slot_block_swapped", "next_block"])
+def test_gather_mutant_caught(bug):
+    checks = [check_paging_fixture, check_gather_contiguous]
+    assert not _fails_some(checks, lambda *a: _gather_variant(*a))
+    assert _fails_some(checks, lambda *a: _gather_variant(*a, bug=bug))
+
+
+def _merge_variant(o_parts, lse_parts, bug):
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    empty = ~np.isfinite(m)
+    ms = np.where(empty, 0.0, m)
+    if bug == "linear_weights":
+        w = np.where(np.isfinite(lse_parts), lse_parts - ms[None] + 1.0, 0.0)
+    elif bug == "weight_sign":
+        w = np.where(np.isfinite(lse_parts), np.exp(ms[None] - lse_parts), 0.0)
+    else:
+        w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - ms[None]), 0.0)
+    ws = w.sum(axis=0)
+    wss = np.where(empty, 1.0, ws)
+    o = (w[..., None] * o_parts).sum(axis=0)
+    if bug != "no_divide":
+        o = o / wss[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, -np.inf, ms + (0.0 if bug == "lse_max_only" else np.log(wss)))
+    return o, lse
+
+
+@pytest.mark.parametrize("bug", ["linear_weights", "weight_sign", "no_divide", "lse_max_only"])
+def test_merge_mutant_caught(bug):
+    def split_check(merge):
+        check_split_merge(oracle.split_partials, merge, 5, 300, True)
+
+    checks = [check_merge_closed_forms, split_check]
+    assert not _fails_some(checks, lambda o, l: _merge_variant(o, l, None))
+    assert _fails_some(checks, lambda o, l: _merge_variant(o, l, bug))
+
+
+def _split_variant(q, k, v, scale, causal, num_splits, block_size=16, bug=None):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    lq, lk = q.shape[0], k.shape[0]
+    vis = oracle.causal_visibility(lq, lk) if causal else np.ones((lq, lk), dtype=bool)
+    op = np.zeros((num_splits, lq, v.shape[1]))
+    lp = np.full((num_splits, lq), -np.inf)
+    for p, (a, b) in enumerate(oracle.split_ranges(lk, num_splits, block_size)):
+        if b <= a:
+            continue
+        if bug == "overlap":
+            a = max(0, a - 1)
+        if bug == "local_causal":
+            sub = oracle.causal_visibility(lq, b - a) if causal else None
+        else:
+            sub = vis[:, a:b]
+        op[p], lp[p] = oracle.masked_attention(q, k[a:b], v[a:b], scale, sub)
+    return op, lp
+
+
+@pytest.mark.parametrize("bug", ["overlap", "local_causal"])
+def test_split_mutant_caught(bug):
+    def run(bugv):
+        def chk(_):
+            check_split_merge(lambda *a: _split_variant(*a, bug=bugv), oracle.lse_merge, 5, 300, True)
+        return chk
+
+    assert not _fails_some([run(None)], None)
+    assert _fails_some([run(bug)], None)
