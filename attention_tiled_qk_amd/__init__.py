@@ -1,0 +1,212 @@
+"""Python face of the gfx950 tiled-attention library.
+
+A thin ctypes binding over the C ABI in ``include/attn.h``: it checks tensor
+placement and layout, allocates outputs with torch (device memory and streams
+are all torch is used for), passes raw pointers and the current HIP stream,
+and raises ``AttnError`` with the library's status text on failure. Every
+step of the computation runs in the HIP kernels; there is no fallback path.
+If the shared library has not been built, importing this package raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+__all__ = [
+    "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
+    "attn_lse_merge", "attn_paged_gather", "attn_version", "lib", "LIB_PATH",
+    "ATTN_F32", "ATTN_BF16",
+]
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m attention_tiled_qk_amd.build "
+        "or __graft_entry__.build()); there is no non-HIP implementation")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+lib.attn_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]
+lib.attn_prefill.restype = _i
+lib.attn_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+lib.attn_paged_workspace_bytes.restype = _sz
+lib.attn_paged_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                  _f, _i, _p, _sz, _i, _p]
+lib.attn_paged_decode.restype = _i
+lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
+lib.attn_lse_merge.restype = _i
+lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
+lib.attn_paged_gather.restype = _i
+lib.attn_status_string.argtypes = [_i]
+lib.attn_status_string.restype = ctypes.c_char_p
+lib.attn_version.argtypes = []
+lib.attn_version.restype = _i
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {lib.attn_status_string(status).decode()} (status {status})")
+
+
+def attn_version():
+    return lib.attn_version()
+
+
+def _check(status, where):
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return ATTN_F32
+    if dt == torch.bfloat16:
+        return ATTN_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def attn_prefill(q, k, v, *, causal=True, scale=None, o=None, lse=None, return_lse=False,
+                 stream=None):
+    """Exact attention of q, k, v [B, H, L, D] (float32 or bfloat16).
+
+    Returns o (and the float32 log-sum-exp [B, H, L] when ``return_lse``).
+    """
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, L, D] of the same shape")
+    B, H, L, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty_like(q)
+    _dev(o, "o", q.dtype)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, L, D,
+                          int(bool(causal)), float(scale), _dtype_code(q.dtype),
+                          _stream(q.device, stream))
+    _check(st, "attn_prefill")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits=0):
+    return int(lib.attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits))
+
+
+def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True, scale=None,
+                      num_splits=0, o=None, lse=None, return_lse=False, workspace=None,
+                      stream=None):
+    """Attention of q [B, H, q_len, D] (bf16) over a paged K/V cache.
+
+    k_pool, v_pool [num_blocks, H, 16, D] bf16; block_tables [B, W] int32;
+    seq_lens [B] int32 (key counts including the q_len new tokens). A float32
+    workspace is allocated here when the split count needs one and none is given.
+    """
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [B, H, q_len, D] and the pools [num_blocks, H, 16, D]")
+    B, H, q_len, D = q.shape
+    nblk, Hp, bs, Dp = k_pool.shape
+    if Hp != H or Dp != D:
+        raise ValueError("pool heads / head_dim must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    width = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, q_len), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    need = attn_paged_workspace_bytes(B, H, q_len, D, width, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.attn_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                               _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, q_len, D, nblk, width,
+                               bs, int(bool(causal)), float(scale), int(num_splits),
+                               _ptr(workspace), ws_bytes, ATTN_BF16, _stream(q.device, stream))
+    _check(st, "attn_paged_decode")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_lse_merge(o_part, lse_part, *, out_dtype=torch.bfloat16, o=None, lse=None,
+                   return_lse=False, stream=None):
+    """Merge o_part [B, H, q_len, S, D] / lse_part [B, H, q_len, S] (float32)."""
+    _dev(o_part, "o_part", torch.float32)
+    _dev(lse_part, "lse_part", torch.float32)
+    if o_part.dim() != 5 or lse_part.shape != o_part.shape[:4]:
+        raise ValueError("o_part must be [B, H, q_len, S, D] and lse_part [B, H, q_len, S]")
+    B, H, q_len, S, D = o_part.shape
+    if o is None:
+        o = torch.empty((B, H, q_len, D), device=o_part.device, dtype=out_dtype)
+    _dev(o, "o")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, q_len), device=o_part.device, dtype=torch.float32)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    st = lib.attn_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, H, q_len, S, D,
+                            _dtype_code(o.dtype), _stream(o_part.device, stream))
+    _check(st, "attn_lse_merge")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, stream=None):
+    """Copy each sequence's valid rows out of pool [N, H, 16, D] (bf16) into
+    out [B, H, max_seq_len, D]; rows past seq_len are left as they were."""
+    _dev(pool, "pool", torch.bfloat16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    nblk, H, bs, D = pool.shape
+    B, width = block_tables.shape
+    if out is None:
+        out = torch.zeros((B, H, max_seq_len, D), device=pool.device, dtype=torch.bfloat16)
+    _dev(out, "out", torch.bfloat16)
+    st = lib.attn_paged_gather(_ptr(pool), _ptr(block_tables), _ptr(seq_lens), _ptr(out), B, H, D,
+                               nblk, width, max_seq_len, _stream(pool.device, stream))
+    _check(st, "attn_paged_gather")
+    return out

@@ -1,0 +1,196 @@
+// Host side of the C ABI declared in include/attn.h: argument validation, the
+// split-count choice for paged decode, and kernel launches on the caller's
+// stream. Everything is checked before anything is enqueued; the library owns
+// no memory and keeps no state besides per-kernel launch attributes.
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attn.h"
+
+namespace attn {
+hipError_t launch_prefill_bf16(const void*, const void*, const void*, void*, float*, int, int, int,
+                               int, int, float, hipStream_t);
+hipError_t launch_prefill_f32(const void*, const void*, const void*, void*, float*, int, int, int,
+                              int, int, float, hipStream_t);
+hipError_t launch_paged_attn(const void*, const void*, const void*, const int32_t*,
+                             const int32_t*, void*, float*, float*, float*, int, int, int, int,
+                             int, int, int, float, hipStream_t);
+hipError_t launch_lse_merge(const float*, const float*, void*, float*, long long, int, int, int,
+                            hipStream_t);
+hipError_t launch_paged_gather(const void*, const int32_t*, const int32_t*, void*, int, int, int,
+                               int, int, hipStream_t);
+}  // namespace attn
+
+namespace {
+
+constexpr long long kMaxGrid = 0x7fffffffLL;
+constexpr int kPrefillRowsBf16 = 128;  // query rows per prefill workgroup (bf16)
+constexpr int kPrefillRowsF32 = 64;
+constexpr int kMaxMergeSplits = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Product of positive ints, or -1 on overflow past 2^62.
+long long checked_mul(std::initializer_list<long long> xs) {
+  long long r = 1;
+  for (long long x : xs) {
+    if (x <= 0) return -1;
+    if (r > (1LL << 62) / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+// Split count for paged decode when the caller leaves it to the library: enough
+// (split, head, sequence) waves to cover the chip several times over, but no
+// split shorter than 16 blocks (256 tokens) on the longest possible sequence.
+int auto_splits(int B, int H, int max_blocks) {
+  const long long waves = (long long)B * H;
+  const long long want = (4096 + waves - 1) / waves;
+  long long cap = max_blocks / 16;
+  if (cap < 1) cap = 1;
+  long long s = want < cap ? want : cap;
+  if (s < 1) s = 1;
+  if (s > ATTN_PAGED_MAX_SPLITS) s = ATTN_PAGED_MAX_SPLITS;
+  return (int)s;
+}
+
+size_t workspace_for(int B, int H, int q_len, int D, int S) {
+  if (S <= 1) return 0;
+  const long long rows = checked_mul({B, H, q_len, S});
+  if (rows < 0) return 0;
+  return (size_t)rows * (size_t)(D + 1) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return ATTN_VERSION; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "a size is non-positive or the shapes disagree";
+    case ATTN_ERR_BAD_DTYPE: return "dtype not supported by this entry point";
+    case ATTN_ERR_UNSUPPORTED: return "head_dim, q_len, block_size or split count is outside the supported set";
+    case ATTN_ERR_MISALIGNED: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_OVERFLOW: return "sizes overflow the kernels' indexing";
+    case ATTN_ERR_HIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int L, int D, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || L <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
+  if (lse && !aligned4(lse)) return ATTN_ERR_MISALIGNED;
+  if (checked_mul({B, H, L, D, 4}) < 0) return ATTN_ERR_OVERFLOW;
+  const int rows = dtype == ATTN_BF16 ? kPrefillRowsBf16 : kPrefillRowsF32;
+  if ((long long)B * H * ((L + rows - 1) / rows) > kMaxGrid) return ATTN_ERR_OVERFLOW;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16)
+    return hip_status(attn::launch_prefill_bf16(q, k, v, o, lse, B, H, L, D, causal, scale, s));
+  return hip_status(attn::launch_prefill_f32(q, k, v, o, lse, B, H, L, D, causal, scale, s));
+}
+
+size_t attn_paged_workspace_bytes(int B, int H, int q_len, int D, int max_blocks_per_seq,
+                                  int num_splits) {
+  if (B <= 0 || H <= 0 || q_len <= 0 || q_len > ATTN_PAGED_MAX_QLEN) return 0;
+  if (D != 64 && D != 128) return 0;
+  if (max_blocks_per_seq <= 0 || num_splits < 0 || num_splits > ATTN_PAGED_MAX_SPLITS) return 0;
+  const int S = num_splits == 0 ? auto_splits(B, H, max_blocks_per_seq) : num_splits;
+  return workspace_for(B, H, q_len, D, S);
+}
+
+int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse,
+                      int B, int H, int q_len, int D, int num_blocks, int max_blocks_per_seq,
+                      int block_size, int causal, float scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !o) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || q_len <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != ATTN_BLOCK_SIZE) return ATTN_ERR_UNSUPPORTED;
+  if (q_len > ATTN_PAGED_MAX_QLEN) return ATTN_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > ATTN_PAGED_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+  if (H > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({num_blocks, H, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
+      (long long)max_blocks_per_seq * 16 > 0x7fffffffLL)
+    return ATTN_ERR_OVERFLOW;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
+    return ATTN_ERR_MISALIGNED;
+  if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
+    return ATTN_ERR_MISALIGNED;
+  const int S = num_splits == 0 ? auto_splits(B, H, max_blocks_per_seq) : num_splits;
+  const size_t need = workspace_for(B, H, q_len, D, S);
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+    o_part = static_cast<float*>(workspace);
+    lse_part = o_part + (size_t)B * H * q_len * S * D;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = attn::launch_paged_attn(q, k_pool, v_pool, block_tables, seq_lens, o, lse, o_part,
+                                         lse_part, B, H, q_len, D, max_blocks_per_seq, S, causal,
+                                         scale, s);
+  if (e != hipSuccess || S == 1) return hip_status(e);
+  return hip_status(attn::launch_lse_merge(o_part, lse_part, o, lse, (long long)B * H * q_len, S, D,
+                                           1, s));
+}
+
+int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int H,
+                   int q_len, int S, int D, int dtype, void* stream) {
+  if (!o_part || !lse_part || !o) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || q_len <= 0 || S <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (S > kMaxMergeSplits) return ATTN_ERR_UNSUPPORTED;
+  const long long rows = checked_mul({B, H, q_len});
+  if (rows < 0 || rows > kMaxGrid || checked_mul({rows, S, D, 4}) < 0) return ATTN_ERR_OVERFLOW;
+  if (!aligned16(o_part) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
+  if (!aligned4(lse_part) || (lse && !aligned4(lse))) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_lse_merge(o_part, lse_part, o, lse, rows, S, D,
+                                           dtype == ATTN_BF16 ? 1 : 0,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32_t* seq_lens,
+                      void* out, int B, int H, int D, int num_blocks, int max_blocks_per_seq,
+                      int max_seq_len, void* stream) {
+  if (!pool || !block_tables || !seq_lens || !out) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (H > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({B, H, max_seq_len, D, 2}) < 0 || checked_mul({num_blocks, H, 16, D, 2}) < 0)
+    return ATTN_ERR_OVERFLOW;
+  if (((long long)max_seq_len * (D / 8) + 255) / 256 > kMaxGrid) return ATTN_ERR_OVERFLOW;
+  if (!aligned16(pool) || !aligned16(out)) return ATTN_ERR_MISALIGNED;
+  if (!aligned4(block_tables) || !aligned4(seq_lens)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_paged_gather(pool, block_tables, seq_lens, out, B, H, D,
+                                              max_blocks_per_seq, max_seq_len,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,336 @@
+// Paged decode / speculative-verify attention, split-KV merge and paged gather.
+//
+// What is computed: for each sequence b and head h, the q_len newest queries
+// attend all seq_len keys of the sequence (bottom-right causal when asked),
+// where token t of the sequence lives in physical block block_tables[b][t/16],
+// slot t%16 of the K and V pools -- PagedAttention's block table as [P1] §3.2
+// draws it and as the Continuous Batching + PagedAttention item of [P3] passes
+// it to the kernel, which reads only the sequence's valid blocks and never the
+// slots past seq_len. Long key ranges are cut into splits handled by separate
+// workgroups, each producing a normalised partial output and its log-sum-exp,
+// and a second kernel merges them (the FlashDecoding item of [P3]).
+//
+// gfx950 mapping: one wave per (split, head, sequence). Keys are consumed two
+// 16-token blocks (32 keys) at a time:
+//   * the K slab of a (block, head) is 16 rows x D contiguous; each lane loads
+//     its 16-byte pieces straight into the A operand of S^T = K Q^T
+//     (v_mfma_f32_16x16x32_bf16; queries, padded to 16, are the N dimension);
+//   * the S^T accumulators hold, per lane, one query and 4 keys of each block,
+//     so row max / sum are 7 in-lane ops plus two permlane swaps;
+//   * P^T goes from those accumulators straight into the B operand of
+//     O^T += V^T P^T; V^T comes from the two V slabs written row-major to a
+//     per-wave LDS area and read back with ds_read_b64_tr_b16;
+//   * block ids are wave-uniform scalar loads; slots past the split's end are
+//     masked in S and zeroed in V (a NaN there must not reach O).
+#include "common.h"
+
+namespace attn {
+
+template <int D>
+__global__ __launch_bounds__(64) void paged_attn_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k_pool, const bf16* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o_part,
+    float* __restrict__ lse_part, int H, int q_len, int max_blocks, int num_splits, int causal,
+    float scale) {
+  constexpr int DC = D / 32;            // 32-wide chunks of the QK^T contraction
+  constexpr int DB = D / 16;            // 16-wide output blocks
+  constexpr int PV = D * 2 + 64;        // LDS row pitch of a V slab (bytes)
+  constexpr int VCH = 16 * D / 8 / 64;  // 16-byte pieces of one slab per lane
+  constexpr int CPR = D / 8;            // 16-byte pieces per slab row
+  __shared__ __attribute__((aligned(16))) unsigned char vlds_raw[2 * 16 * PV];
+  ATTN_LDS unsigned char* vlds = (ATTN_LDS unsigned char*)vlds_raw;
+
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+
+  const int seq_len = seq_lens[b];
+  const int nb = (seq_len + 15) >> 4;
+  const int per = (nb + num_splits - 1) / num_splits;
+  const int blk0 = min(split * per, nb);
+  const int blk1 = min(blk0 + per, nb);
+  const int key_end = min(seq_len, blk1 * 16);
+  const int qpos0 = seq_len - q_len;  // absolute position of query 0
+  const int limit = causal ? qpos0 + l16 : 0x7fffffff;  // last key my query may see
+
+  const size_t bhq = ((size_t)b * H + h) * q_len;  // row of (b, h, query 0)
+
+  if (blk0 >= blk1) {  // empty split: contributes nothing to the merge
+    if (l16 < q_len) {
+      if (num_splits == 1) {  // only for seq_len == 0, outside the contract
+        bf16* dst = o + (bhq + l16) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<u32x2*>(dst + db * 16 + 4 * g) = u32x2{0u, 0u};
+        if (lse != nullptr && g == 0) lse[bhq + l16] = -INFINITY;
+      } else {
+        float* dst = o_part + ((bhq + l16) * num_splits + split) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (g == 0) lse_part[(bhq + l16) * num_splits + split] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  // Q as the B operand: lane holds query l16, d = 32 c + 8 g + (0..7)
+  bf16x8 qreg[DC];
+  {
+    const bool ok = l16 < q_len;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + (bhq + (ok ? l16 : 0)) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      u32x4 w = ok ? src[c * 4] : u32x4{0, 0, 0, 0};
+      qreg[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const size_t blk_stride = (size_t)H * 16 * D;  // elements per physical block
+  const size_t head_off = (size_t)h * 16 * D;
+  const int32_t* table = block_tables + (size_t)b * max_blocks;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float cs = scale * kLog2e;
+
+  for (int n = blk0; n < blk1; n += 2) {
+    const bool has_b = n + 1 < blk1;
+    const int pa = table[n];
+    const int pb = has_b ? table[n + 1] : pa;
+    const bf16* ka_src = k_pool + (size_t)pa * blk_stride + head_off;
+    const bf16* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
+    const bf16* va_src = v_pool + (size_t)pa * blk_stride + head_off;
+    const bf16* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
+
+    // K operands (row l16 of the slab) and V pieces (contiguous per instruction)
+    bf16x8 ka[DC], kb[DC];
+    u32x4 va[VCH], vb[VCH];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      ka[c] = *reinterpret_cast<const bf16x8*>(ka_src + l16 * D + 32 * c + 8 * g);
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) va[i] = *reinterpret_cast<const u32x4*>(va_src + (i * 64 + lane) * 8);
+    if (has_b) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        kb[c] = *reinterpret_cast<const bf16x8*>(kb_src + l16 * D + 32 * c + 8 * g);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) vb[i] = *reinterpret_cast<const u32x4*>(vb_src + (i * 64 + lane) * 8);
+    } else {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) kb[c] = bf16x8{};
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) vb[i] = u32x4{0, 0, 0, 0};
+    }
+
+    const int key0 = n * 16;
+    const bool tail = key0 + 32 > key_end;
+    if (tail) {  // V rows at or past the split's end must be exactly zero
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int row = (i * 64 + lane) / CPR;
+        if (key0 + row >= key_end) va[i] = u32x4{0, 0, 0, 0};
+        if (key0 + 16 + row >= key_end) vb[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+
+    // S^T[key][query] for both blocks
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      sa = mfma16(ka[c], qreg[c], sa);
+      sb = mfma16(kb[c], qreg[c], sb);
+    }
+
+    if (tail || (causal && key0 + 31 > qpos0)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kA = key0 + 4 * g + j;
+        const int kB = kA + 16;
+        sa[j] = (kA < key_end && kA <= limit) ? sa[j] : -INFINITY;
+        sb[j] = (kB < key_end && kB <= limit) ? sb[j] : -INFINITY;
+      }
+    }
+
+    float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                     fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+    mt = max_xor16(mt);
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      // lanes whose max did not move keep alpha = 1 (also avoids -inf - -inf)
+      const float alpha = m_new == m_run ? 1.f : exp2_fast((m_run - m_new) * cs);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * cs;
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = exp2_fast(__builtin_fmaf(sa[j], cs, -mc));
+      e[4 + j] = exp2_fast(__builtin_fmaf(sb[j], cs, -mc));
+    }
+    l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    u32x4 pw;
+    pw[0] = pack_bf16x2(e[0], e[1]);
+    pw[1] = pack_bf16x2(e[2], e[3]);
+    pw[2] = pack_bf16x2(e[4], e[5]);
+    pw[3] = pack_bf16x2(e[6], e[7]);
+    const bf16x8 p = __builtin_bit_cast(bf16x8, pw);
+
+    // V slabs -> LDS (row-major, padded rows), then transposing reads
+    __syncthreads();  // previous pair's reads are done before overwriting
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int piece = i * 64 + lane;
+      const int row = piece / CPR;
+      const int col = piece % CPR;
+      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 16) = va[i];
+      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 16) = vb[i];
+    }
+    __syncthreads();
+    const ATTN_LDS unsigned char* rd = vlds + (4 * g + (l16 >> 2)) * PV + 8 * (l16 & 3);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x4 lo = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(rd + db * 32));
+      const bf16x4 hi = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(rd + 16 * PV + db * 32));
+      acc[db] = mfma16(join(lo, hi), p, acc[db]);
+    }
+  }
+
+  // ---- epilogue
+  float l_tot = sum_xor16(l_run);
+  l_tot = sum_xor32(l_tot);
+  if (l16 < q_len) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float row_lse = l_tot > 0.f ? scale * m_run + __logf(l_tot) : -INFINITY;
+    if (num_splits == 1) {
+      bf16* dst = o + (bhq + l16) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
+        w[1] = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
+        *reinterpret_cast<u32x2*>(dst + db * 16 + 4 * g) = w;
+      }
+      if (lse != nullptr && g == 0) lse[bhq + l16] = row_lse;
+    } else {
+      float* dst = o_part + ((bhq + l16) * num_splits + split) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = acc[db] * inv;
+      if (g == 0) lse_part[(bhq + l16) * num_splits + split] = row_lse;
+    }
+  }
+}
+
+// Cross-split reduction: one workgroup of D threads per output row.
+template <int D, typename OutT>
+__global__ __launch_bounds__(D) void lse_merge_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part,
+                                                      OutT* __restrict__ o, float* __restrict__ lse,
+                                                      int S) {
+  const size_t row = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* lp = lse_part + row * S;
+  float m = -INFINITY;
+  for (int p = 0; p < S; ++p) m = fmaxf(m, lp[p]);
+  float acc = 0.f, wsum = 0.f;
+  if (m != -INFINITY) {
+    const float* op = o_part + row * S * D + d;
+    for (int p = 0; p < S; ++p) {
+      const float lv = lp[p];
+      const float w = lv == -INFINITY ? 0.f : expf(lv - m);
+      wsum += w;
+      acc = __builtin_fmaf(w, op[(size_t)p * D], acc);
+    }
+  }
+  const float out = wsum > 0.f ? acc / wsum : 0.f;
+  o[row * D + d] = (OutT)out;
+  if (lse != nullptr && d == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+}
+
+// Bit-exact copy of each sequence's valid rows out of the pool.
+template <int D>
+__global__ __launch_bounds__(256) void paged_gather_kernel(const bf16* __restrict__ pool,
+                                                           const int32_t* __restrict__ block_tables,
+                                                           const int32_t* __restrict__ seq_lens,
+                                                           bf16* __restrict__ out, int H,
+                                                           int max_blocks, int max_seq_len) {
+  constexpr int CPR = D / 8;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n = min(seq_lens[b], max_seq_len);
+  const long long piece = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int t = (int)(piece / CPR);
+  const int c = (int)(piece % CPR);
+  if (t >= n) return;
+  const int phys = block_tables[(size_t)b * max_blocks + (t >> 4)];
+  const size_t src = (((size_t)phys * H + h) * 16 + (t & 15)) * D + c * 8;
+  const size_t dst = (((size_t)b * H + h) * max_seq_len + t) * D + c * 8;
+  *reinterpret_cast<u32x4*>(out + dst) = *reinterpret_cast<const u32x4*>(pool + src);
+}
+
+hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                             float* lse, float* o_part, float* lse_part, int B, int H, int q_len,
+                             int D, int max_blocks, int num_splits, int causal, float scale,
+                             hipStream_t stream) {
+  dim3 grid(num_splits, H, B);
+  if (D == 128)
+    hipLaunchKernelGGL(paged_attn_kernel<128>, grid, dim3(64), 0, stream, (const bf16*)q,
+                       (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
+                       lse, o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+  else
+    hipLaunchKernelGGL(paged_attn_kernel<64>, grid, dim3(64), 0, stream, (const bf16*)q,
+                       (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
+                       lse, o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                            long long rows, int S, int D, int out_bf16, hipStream_t stream) {
+  dim3 grid((unsigned)rows);
+  if (D == 128) {
+    if (out_bf16)
+      hipLaunchKernelGGL((lse_merge_kernel<128, bf16>), grid, dim3(128), 0, stream, o_part,
+                         lse_part, (bf16*)o, lse, S);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<128, float>), grid, dim3(128), 0, stream, o_part,
+                         lse_part, (float*)o, lse, S);
+  } else {
+    if (out_bf16)
+      hipLaunchKernelGGL((lse_merge_kernel<64, bf16>), grid, dim3(64), 0, stream, o_part,
+                         lse_part, (bf16*)o, lse, S);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<64, float>), grid, dim3(64), 0, stream, o_part,
+                         lse_part, (float*)o, lse, S);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_gather(const void* pool, const int32_t* block_tables,
+                               const int32_t* seq_lens, void* out, int B, int H, int D,
+                               int max_blocks, int max_seq_len, hipStream_t stream) {
+  const long long pieces = (long long)max_seq_len * (D / 8);
+  dim3 grid((unsigned)((pieces + 255) / 256), H, B);
+  if (D == 128)
+    hipLaunchKernelGGL(paged_gather_kernel<128>, grid, dim3(256), 0, stream, (const bf16*)pool,
+                       block_tables, seq_lens, (bf16*)out, H, max_blocks, max_seq_len);
+  else
+    hipLaunchKernelGGL(paged_gather_kernel<64>, grid, dim3(256), 0, stream, (const bf16*)pool,
+                       block_tables, seq_lens, (bf16*)out, H, max_blocks, max_seq_len);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,119 @@
+// Prefill attention for float32 Q, K, V (the exact-precision path).
+//
+// Same method as the bf16 kernel -- tiling with the online softmax of [P1]
+// §2.2, K/V tiles staged in LDS, running max m and exp-sum l per row, one
+// division by l after the last tile -- computed in float32 on the vector ALUs
+// with accurate expf, because float32 inputs are held to a 1e-5 bound that
+// bf16 matrix-core operands cannot meet. Each query row is owned by two lanes
+// (one half of the head dimension each); a workgroup covers 64 rows and walks
+// 32-key tiles.
+#include "common.h"
+
+namespace attn {
+
+namespace {
+constexpr int F_BM = 64;  // query rows per workgroup
+constexpr int F_BN = 32;  // keys per tile
+}  // namespace
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restrict__ q,
+                                                          const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          float* __restrict__ o,
+                                                          float* __restrict__ lse, int L,
+                                                          int n_qtiles, float scale) {
+  constexpr int HD = D / 2;
+  constexpr int PITCH = D + 4;
+  __shared__ float ks[F_BN * PITCH];
+  __shared__ float vs[F_BN * PITCH];
+
+  const int tid = threadIdx.x;
+  const int half = tid & 1;
+  const int bh = blockIdx.x / n_qtiles;
+  const int qt = blockIdx.x % n_qtiles;
+  const int row = qt * F_BM + (tid >> 1);
+  const size_t head_off = (size_t)bh * L * D;
+
+  float qr[HD], acc[HD];
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    qr[d] = row < L ? q[head_off + (size_t)row * D + half * HD + d] : 0.f;
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  const int n_all = (L + F_BN - 1) / F_BN;
+  const int n_kt = CAUSAL ? min(n_all, (min(qt * F_BM + F_BM, L) - 1) / F_BN + 1) : n_all;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    for (int i = tid; i < F_BN * D; i += 128) {
+      const int r = i / D, d = i % D;
+      const int key = kt * F_BN + r;
+      ks[r * PITCH + d] = key < L ? k[head_off + (size_t)key * D + d] : 0.f;
+      vs[r * PITCH + d] = key < L ? v[head_off + (size_t)key * D + d] : 0.f;
+    }
+    __syncthreads();
+
+    float s[F_BN];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < F_BN; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) part = __builtin_fmaf(qr[d], ks[j * PITCH + half * HD + d], part);
+      const float full = part + __shfl_xor(part, 1);
+      const int key = kt * F_BN + j;
+      const bool vis = key < L && (!CAUSAL || key <= row);
+      s[j] = vis ? full * scale : -INFINITY;
+      mt = fmaxf(mt, s[j]);
+    }
+    const float m_new = fmaxf(m, mt);
+    if (m_new != -INFINITY) {
+      const float alpha = m == -INFINITY ? 0.f : expf(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) acc[d] *= alpha;
+#pragma unroll
+      for (int j = 0; j < F_BN; ++j) {
+        const float p = s[j] == -INFINITY ? 0.f : expf(s[j] - m_new);
+        l += p;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) acc[d] = __builtin_fmaf(p, vs[j * PITCH + half * HD + d], acc[d]);
+      }
+      m = m_new;
+    }
+  }
+
+  if (row < L) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) o[head_off + (size_t)row * D + half * HD + d] = acc[d] * inv;
+    if (lse != nullptr && half == 0) lse[(size_t)bh * L + row] = l > 0.f ? m + logf(l) : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int L, float scale, hipStream_t stream) {
+  const int n_qtiles = (L + F_BM - 1) / F_BM;
+  const long long grid = (long long)B * H * n_qtiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(128), 0, stream,
+                     (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, L,
+                     n_qtiles, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int L, int D, int causal, float scale,
+                              hipStream_t stream) {
+  if (D == 128)
+    return causal ? launch_f32<128, true>(q, k, v, o, lse, B, H, L, scale, stream)
+                  : launch_f32<128, false>(q, k, v, o, lse, B, H, L, scale, stream);
+  return causal ? launch_f32<64, true>(q, k, v, o, lse, B, H, L, scale, stream)
+                : launch_f32<64, false>(q, k, v, o, lse, B, H, L, scale, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,186 @@
+/*
+ * attn.h -- C ABI of the gfx950 (MI355X) tiled-attention library.
+ *
+ * Exact attention O = softmax(scale * Q K^T + mask) V computed IO-aware: the
+ * score matrix is formed tile by tile on chip and folded into a running row
+ * maximum m and exponential sum l (online softmax), so it never reaches HBM.
+ * Sources, cited by page and section:
+ *   [P1] iopencloud.com, "大模型推理加速技术全景：从FlashAttention到Speculative
+ *        Decoding": §2.1 standard attention, §2.2 tiling and online softmax,
+ *        §3.2 PagedAttention (16-token block pool and per-request page tables).
+ *   [P2] ybb.press/llm-inference/15723.html: §一 the scaled dot-product
+ *        attention formula softmax(QK^T / sqrt(d_k)) V.
+ *   [P3] lowentro.cn notes "推理加速技术": the FlashAttention core-idea item,
+ *        the FlashAttention-2 item, the FlashDecoding item (split the key range
+ *        across workgroups, then a cross-split reduction kernel), and the
+ *        Continuous Batching + PagedAttention item (the kernel receives each
+ *        request's block table and reads only valid blocks).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or synchronises; it enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and returns. Results are ready
+ *     when the stream reaches that point.
+ *   - Layouts are dense, row-major, innermost dimension last, as stated per
+ *     argument. Pointers must be 16-byte aligned.
+ *   - dtype: ATTN_F32 = float32, ATTN_BF16 = bfloat16. Accumulation is float32.
+ *   - Causal masking is bottom-right aligned: with Lq queries over Lk keys,
+ *     query t sits at position Lk - Lq + t and sees keys 0 .. Lk - Lq + t.
+ *   - lse outputs are the natural-log log-sum-exp of the scaled scores of each
+ *     query row (float32); a row that sees no key gets -inf and a zero output.
+ *   - Every argument is validated on the host before anything is enqueued. On
+ *     error the call returns a negative ATTN_ERR_* code and enqueues nothing.
+ *     Device-side contents are trusted: block ids outside [0, num_blocks) or
+ *     seq_lens above max_blocks_per_seq * 16 are undefined behaviour.
+ *   - Calls are stateless and re-entrant; calls on different streams may run
+ *     concurrently if their output buffers do not overlap.
+ */
+#ifndef ATTN_TILED_QK_H
+#define ATTN_TILED_QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_VERSION 100 /* 1.0.0 */
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+  ATTN_ERR_BAD_SHAPE = -2,   /* a size is zero/negative or shapes disagree */
+  ATTN_ERR_BAD_DTYPE = -3,   /* dtype not supported by this entry point */
+  ATTN_ERR_UNSUPPORTED = -4, /* head_dim, q_len, block_size or split count outside the supported set */
+  ATTN_ERR_MISALIGNED = -5,  /* a pointer is not 16-byte aligned */
+  ATTN_ERR_WORKSPACE = -6,   /* workspace missing or smaller than attn_paged_workspace_bytes() */
+  ATTN_ERR_OVERFLOW = -7,    /* an element count does not fit the kernels' 32/64-bit indexing */
+  ATTN_ERR_HIP = -8          /* the kernel launch itself failed (hipGetLastError) */
+};
+
+/* Largest query count per sequence accepted by attn_paged_decode. */
+#define ATTN_PAGED_MAX_QLEN 16
+/* Largest explicit split count accepted by attn_paged_decode. */
+#define ATTN_PAGED_MAX_SPLITS 64
+/* The only KV block size supported (tokens per physical block). */
+#define ATTN_BLOCK_SIZE 16
+
+/*
+ * attn_prefill -- exact attention for a batch of full sequences
+ *                 ([P1] §2.2 tiling + online softmax, [P2] §一 formula).
+ *
+ *   q, k, v : [B, H, L, D] of `dtype`, contiguous.
+ *   o       : [B, H, L, D] of `dtype` (written). May not alias q, k or v.
+ *   lse     : [B, H, L] float32 (written), or NULL to skip it.
+ *   B, H, L : batch, heads, sequence length (>= 1).
+ *   D       : head dimension, 64 or 128.
+ *   causal  : 0 = full attention, 1 = causal (query i sees keys 0..i).
+ *   scale   : multiplier of Q K^T (normally 1/sqrt(D)); finite.
+ *   dtype   : ATTN_F32 or ATTN_BF16.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int L, int D, int causal, float scale, int dtype,
+                 void* stream);
+
+/*
+ * attn_paged_workspace_bytes -- size of the float32 scratch that
+ * attn_paged_decode needs for `num_splits` split-KV partials: the normalised
+ * partial outputs [B, H, q_len, S, D] and their lse [B, H, q_len, S].
+ * num_splits = 0 asks for the split count the library would choose itself for
+ * the given max_blocks_per_seq. Returns 0 when one split suffices (no
+ * workspace needed) and also for invalid arguments.
+ */
+size_t attn_paged_workspace_bytes(int B, int H, int q_len, int D, int max_blocks_per_seq,
+                                  int num_splits);
+
+/*
+ * attn_paged_decode -- attention of q_len new queries per sequence over a
+ * PagedAttention KV cache ([P1] §3.2, [P3] block tables in the kernel), with
+ * optional FlashDecoding split-KV ([P3]) and log-sum-exp merge.
+ *
+ *   q            : [B, H, q_len, D] bf16, contiguous.
+ *   k_pool,
+ *   v_pool       : [num_blocks, H, 16, D] bf16: physical block p, head h, slot s
+ *                  holds the key/value of the token stored there.
+ *   block_tables : [B, max_blocks_per_seq] int32 device array: entry n of row b
+ *                  is the physical block holding tokens 16n .. 16n+15 of
+ *                  sequence b. Entries at or past ceil(seq_lens[b] / 16) are
+ *                  never read (pad with -1).
+ *   seq_lens     : [B] int32 device array: the key count of each sequence,
+ *                  INCLUDING its q_len new tokens (already written to the cache).
+ *                  Must satisfy q_len <= seq_lens[b] <= max_blocks_per_seq * 16.
+ *                  Slots past seq_len in the last block are never read.
+ *   o            : [B, H, q_len, D] bf16 (written).
+ *   lse          : [B, H, q_len] float32 (written), or NULL.
+ *   q_len        : 1 .. ATTN_PAGED_MAX_QLEN (1 = decode; K+1 = speculative verify).
+ *   D            : 128 (64 also accepted).
+ *   block_size   : must be 16.
+ *   causal       : 1 = bottom-right causal within the new tokens (query t sees
+ *                  keys 0 .. seq_len - q_len + t); 0 = all seq_len keys.
+ *   num_splits   : 0 = library's choice; else 1 .. ATTN_PAGED_MAX_SPLITS. With S
+ *                  splits, sequence b's ceil(seq_len/16) blocks are cut into S
+ *                  contiguous ranges of ceil(nb/S) blocks; each is attended
+ *                  independently and the partials are merged.
+ *   workspace    : device scratch of at least attn_paged_workspace_bytes(B, H,
+ *                  q_len, D, max_blocks_per_seq, num_splits) bytes (may be NULL
+ *                  when that is 0). Contents on entry are ignored.
+ *   dtype        : must be ATTN_BF16.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                      float* lse, int B, int H, int q_len, int D, int num_blocks,
+                      int max_blocks_per_seq, int block_size, int causal, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes, int dtype,
+                      void* stream);
+
+/*
+ * attn_lse_merge -- the FlashDecoding cross-split reduction ([P3]): combine S
+ * softmax-normalised partial outputs with their log-sum-exps. For each row,
+ * M = max_p lse_p, w_p = exp(lse_p - M), o = sum_p w_p o_p / sum_p w_p and
+ * lse = M + log(sum_p w_p) -- the rescaling step of the online softmax of
+ * [P1] §2.2 applied across splits. Rows whose partials are all -inf get o = 0
+ * and lse = -inf.
+ *
+ *   o_part   : [B, H, q_len, S, D] float32.
+ *   lse_part : [B, H, q_len, S] float32 (-inf marks an empty partial).
+ *   o        : [B, H, q_len, D] of `dtype` (ATTN_F32 or ATTN_BF16), written.
+ *   lse      : [B, H, q_len] float32, written, or NULL.
+ *   S        : 1 .. 1024.  D: 64 or 128.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                   int B, int H, int q_len, int S, int D, int dtype, void* stream);
+
+/*
+ * attn_paged_gather -- copy each sequence's cached rows out of a paged pool
+ * into a contiguous tensor, through its block table ([P1] §3.2). Bit-exact
+ * copy; used to check block-table indexing.
+ *
+ *   pool         : [num_blocks, H, 16, D] bf16.
+ *   block_tables : [B, max_blocks_per_seq] int32 device.
+ *   seq_lens     : [B] int32 device, each <= min(max_seq_len, max_blocks_per_seq*16).
+ *   out          : [B, H, max_seq_len, D] bf16; rows t < seq_lens[b] are
+ *                  written, the rest are left untouched.
+ *   D            : 64 or 128.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32_t* seq_lens,
+                      void* out, int B, int H, int D, int num_blocks, int max_blocks_per_seq,
+                      int max_seq_len, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* attn_status_string(int status);
+
+/* ATTN_VERSION of the built library. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_TILED_QK_H */

@@ -1,0 +1,148 @@
+"""CPU checks of the C ABI: the library loads, exports what include/attn.h
+declares, and rejects bad arguments on the host before touching a device.
+
+No call here reaches a kernel launch: each one fails validation first (the
+pointers passed are fake but never dereferenced), so these run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def api():
+    import attention_tiled_qk_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def header_constants():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"(ATTN_[A-Z_0-9]+)\s*=\s*(-?\d+)", text)}
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["attn_prefill", "attn_paged_decode", "attn_lse_merge", "attn_paged_gather",
+              "attn_paged_workspace_bytes", "attn_status_string", "attn_version"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(api):
+    for name in declared_functions():
+        assert hasattr(api.lib, name), name
+
+
+def test_version(api):
+    assert api.attn_version() == 100
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 4)
+
+
+def test_status_strings(api):
+    c = header_constants()
+    for name, val in c.items():
+        if name.startswith("ATTN_ERR_") or name == "ATTN_OK":
+            s = api.lib.attn_status_string(val).decode()
+            assert s and s != "unknown status"
+    assert api.lib.attn_status_string(12345).decode() == "unknown status"
+
+
+def test_prefill_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+    ok = dict(B=1, H=1, Lq=128, D=64, causal=1, scale=0.125, dtype=0)
+
+    def call(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, **kw):
+        a = dict(ok, **kw)
+        return L.attn_prefill(q, k, v, o, lse, a["B"], a["H"], a["Lq"], a["D"], a["causal"],
+                              a["scale"], a["dtype"], None)
+
+    assert call(q=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(o=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(B=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(Lq=-3) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(D=96) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(D=256) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(dtype=7) == c["ATTN_ERR_BAD_DTYPE"]
+    assert call(causal=2) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(scale=float("nan")) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(scale=float("inf")) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(k=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+    assert call(B=1 << 20, H=1 << 20, Lq=1 << 20, D=128) == c["ATTN_ERR_OVERFLOW"]
+
+
+def test_paged_decode_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+    base = dict(B=2, H=4, q_len=1, D=128, nblk=10, width=8, bs=16, causal=1, scale=0.1,
+                splits=1, ws=None, ws_bytes=0, dtype=1)
+
+    def call(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=None, **kw):
+        a = dict(base, **kw)
+        return L.attn_paged_decode(q, kp, vp, bt, sl, o, lse, a["B"], a["H"], a["q_len"], a["D"],
+                                   a["nblk"], a["width"], a["bs"], a["causal"], a["scale"],
+                                   a["splits"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+    assert call(bt=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(sl=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(B=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(nblk=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(dtype=0) == c["ATTN_ERR_BAD_DTYPE"]
+    assert call(bs=32) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(q_len=17) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(q_len=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(D=80) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(splits=65) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(splits=-1) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(o=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+    assert call(H=70000) == c["ATTN_ERR_OVERFLOW"]
+    # a split count above one needs a workspace of the advertised size
+    need = L.attn_paged_workspace_bytes(2, 4, 1, 128, 8, 4)
+    assert need == 4 * 2 * 4 * 1 * 4 * (128 + 1)
+    assert call(splits=4) == c["ATTN_ERR_WORKSPACE"]
+    assert call(splits=4, ws=FAKE, ws_bytes=need - 4) == c["ATTN_ERR_WORKSPACE"]
+
+
+def test_workspace_bytes(api):
+    L = api.lib
+    assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 16) == 4 * 4 * 40 * 5 * 16 * 129
+    assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 1) == 0
+    assert L.attn_paged_workspace_bytes(0, 40, 5, 128, 2048, 16) == 0
+    assert L.attn_paged_workspace_bytes(4, 40, 17, 128, 2048, 16) == 0
+    # automatic split count: never more than one split per 16 blocks
+    assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 15, 0) == 0
+    auto = L.attn_paged_workspace_bytes(1, 1, 1, 128, 256, 0)
+    assert auto == 4 * 16 * 129
+
+
+def test_merge_and_gather_reject_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+    assert L.attn_lse_merge(None, FAKE, FAKE, None, 1, 1, 1, 2, 128, 1, None) == c["ATTN_ERR_NULL_PTR"]
+    assert L.attn_lse_merge(FAKE, FAKE, FAKE, None, 1, 1, 1, 0, 128, 1, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_lse_merge(FAKE, FAKE, FAKE, None, 1, 1, 1, 2000, 128, 1, None) == c["ATTN_ERR_UNSUPPORTED"]
+    assert L.attn_lse_merge(FAKE, FAKE, FAKE, None, 1, 1, 1, 2, 128, 5, None) == c["ATTN_ERR_BAD_DTYPE"]
+    assert L.attn_paged_gather(FAKE, FAKE, FAKE, None, 1, 1, 128, 4, 4, 64, None) == c["ATTN_ERR_NULL_PTR"]
+    assert L.attn_paged_gather(FAKE, FAKE, FAKE, FAKE, 1, 1, 100, 4, 4, 64, None) == c["ATTN_ERR_UNSUPPORTED"]
+    assert L.attn_paged_gather(FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 4, 4, 0, None) == c["ATTN_ERR_BAD_SHAPE"]
+
+
+def test_binding_refuses_cpu_tensors(api):
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        api.attn_prefill(x, x, x)

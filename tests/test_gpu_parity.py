@@ -1,0 +1,320 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Tolerances (max abs error over all compared elements):
+  * float32 prefill: 1e-5 on O.
+  * bfloat16 paths: 2e-2 on O (fp32 accumulation; the output rounding to bf16
+    alone is up to 2^-8 |O|), 1e-3 on the float32 log-sum-exp.
+  * block-table indexing (gather): bit-exact; paged outputs bit-identical under
+    a permutation of the physical blocks.
+Full-size workloads are checked on sampled (batch, head) pairs that the oracle
+evaluates one by one, in the launch configuration the benchmark times.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import (C1, C2, C3, C4, C5, PagedInputs, PagedSpec, PrefillSpec, paged_inputs,
+                       permute_pool, prefill_inputs)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module")
+def api():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_tiled_qk_amd as m
+    return m
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(*ts):
+    return [t.cuda() for t in ts]
+
+
+def max_err(gpu, ref, pairs=None):
+    g = gpu.detach().double().cpu().numpy()
+    if pairs is None:
+        return float(np.abs(g - ref).max())
+    return max(float(np.abs(g[b, h] - ref[b, h]).max()) for b, h in pairs)
+
+
+def lse_err(gpu, ref, pairs=None):
+    g = gpu.detach().double().cpu().numpy()
+    if pairs is not None:
+        g = np.stack([g[b, h] for b, h in pairs])
+        ref = np.stack([ref[b, h] for b, h in pairs])
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    return float(np.abs(g[fin] - ref[fin]).max()) if fin.any() else 0.0
+
+
+def test_device_report():
+    p = torch.cuda.get_device_properties(0)
+    say(f"device: {p.name} arch={getattr(p, 'gcnArchName', '?')} CUs={p.multi_processor_count} "
+        f"mem={p.total_memory / 2**30:.0f} GiB")
+
+
+# ------------------------------------------------------------------ prefill ---
+
+PREFILL_SMALL = [
+    PrefillSpec("f32_c1_shape", 1, 1, 128, 64, "f32", True, 1),
+    PrefillSpec("f32_ragged_full_d128", 2, 2, 200, 128, "f32", False, 11),
+    PrefillSpec("f32_L1", 1, 3, 1, 64, "f32", True, 12),
+    PrefillSpec("f32_ragged_causal_d64", 1, 2, 333, 64, "f32", True, 13),
+    PrefillSpec("bf16_ragged_causal", 2, 3, 300, 128, "bf16", True, 21),
+    PrefillSpec("bf16_ragged_full", 2, 3, 300, 128, "bf16", False, 22),
+    PrefillSpec("bf16_L1", 1, 2, 1, 128, "bf16", True, 23),
+    PrefillSpec("bf16_L17_d64", 1, 2, 17, 64, "bf16", True, 24),
+    PrefillSpec("bf16_513_full_d64", 1, 1, 513, 64, "bf16", False, 25),
+    PrefillSpec("bf16_129_causal", 3, 2, 129, 128, "bf16", True, 26),
+    PrefillSpec("bf16_1024_causal", 1, 2, 1024, 128, "bf16", True, 27),
+]
+
+
+@pytest.mark.parametrize("spec", PREFILL_SMALL, ids=lambda s: s.name)
+def test_prefill_small(api, spec):
+    say(f"prefill {spec}")
+    q, k, v = prefill_inputs(spec)
+    ref_o, ref_lse = oracle.prefill(q, k, v, spec.scale, spec.causal)
+    dq, dk, dv = to_dev(q, k, v)
+    o, lse = api.attn_prefill(dq, dk, dv, causal=spec.causal, scale=spec.scale, return_lse=True)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if spec.dtype == "f32" else TOL_BF16
+    e = max_err(o, ref_o)
+    el = lse_err(lse, ref_lse)
+    say(f"  max|dO|={e:.3e} (tol {tol}) max|dlse|={el:.3e}")
+    assert e <= tol
+    assert el <= (TOL_F32 if spec.dtype == "f32" else TOL_LSE)
+
+
+def test_prefill_c1_exact_config(api):
+    q, k, v = prefill_inputs(C1)
+    ref, _ = oracle.prefill(q, k, v, C1.scale, C1.causal)
+    o = api.attn_prefill(*to_dev(q, k, v), causal=True, scale=C1.scale)
+    e = max_err(o, ref)
+    say(f"c1: max|dO|={e:.3e}")
+    assert e <= TOL_F32
+
+
+@pytest.mark.parametrize("spec,pairs", [
+    (C2, [(0, 0), (3, 7), (7, 15), (5, 2)]),
+    (C3, [(0, 0), (0, 17), (0, 39)]),
+], ids=["c2", "c3"])
+def test_prefill_full_size_sampled(api, spec, pairs):
+    say(f"full-size {spec.name}, oracle on {pairs}")
+    q, k, v = prefill_inputs(spec)
+    ref_o, ref_lse = oracle.prefill(q, k, v, spec.scale, spec.causal, heads=pairs)
+    o, lse = api.attn_prefill(*to_dev(q, k, v), causal=spec.causal, scale=spec.scale,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    e = max_err(o, ref_o, pairs)
+    el = lse_err(lse, ref_lse, pairs)
+    say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_LSE
+    assert torch.isfinite(o.float()).all()
+
+
+def test_prefill_deterministic(api):
+    q, k, v = to_dev(*prefill_inputs(PrefillSpec("d", 2, 2, 300, 128, "bf16", True, 5)))
+    o1 = api.attn_prefill(q, k, v)
+    o2 = api.attn_prefill(q, k, v)
+    assert torch.equal(o1, o2)
+
+
+# -------------------------------------------------------------------- paged ---
+
+def _paged(lens, q_len, H=3, D=128, seed=0, extra=4, prefix=0, poison=True):
+    """Paged inputs with explicit lengths (NaN in every slot no table may read)."""
+    g = torch.Generator().manual_seed(seed)
+    nb = [-(-n // 16) for n in lens]
+    own = [n - prefix for n in nb]
+    total = prefix + sum(own) + extra
+    perm = torch.randperm(total, generator=g)
+    width = max(nb) + 2
+    tables = torch.full((len(lens), width), -1, dtype=torch.int32)
+    pos = prefix
+    for b in range(len(lens)):
+        row = torch.cat([perm[:prefix], perm[pos:pos + own[b]]])
+        pos += own[b]
+        tables[b, :row.numel()] = row.to(torch.int32)
+    k_pool = torch.randn(total, H, 16, D, generator=g).to(torch.bfloat16)
+    v_pool = torch.randn(total, H, 16, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(len(lens), H, q_len, D, generator=g).to(torch.bfloat16)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    if poison:
+        readable = torch.zeros(total, 16, dtype=torch.bool)
+        for b, n in enumerate(lens):
+            for t in range(n):
+                readable[int(tables[b, t // 16]), t % 16] = True
+        idx = (~readable).nonzero(as_tuple=True)
+        k_pool[idx[0], :, idx[1], :] = float("nan")
+        v_pool[idx[0], :, idx[1], :] = float("nan")
+    return PagedInputs(q, k_pool, v_pool, tables, lens_t)
+
+
+def _run_paged(api, inp, splits, causal=True, scale=None):
+    D = inp.q.shape[3]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    dq, dk, dv, dt, dl = to_dev(inp.q, inp.k_pool, inp.v_pool, inp.block_tables, inp.seq_lens)
+    o, lse = api.attn_paged_decode(dq, dk, dv, dt, dl, causal=causal, scale=scale,
+                                   num_splits=splits, return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+PAGED_CASES = [
+    ((1, 16, 17, 100, 257, 1000), 1),
+    ((5, 16, 17, 100, 257, 1000), 5),
+    ((16, 17, 33, 100, 257, 1000), 16),
+    ((31, 48, 49), 3),
+]
+
+
+@pytest.mark.parametrize("lens,q_len", PAGED_CASES)
+@pytest.mark.parametrize("splits", [1, 2, 3, 16, 0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_small(api, lens, q_len, splits, causal):
+    say(f"paged lens={lens} q_len={q_len} splits={splits} causal={causal}")
+    inp = _paged(lens, q_len, seed=len(lens) * 31 + q_len)
+    scale = 1.0 / math.sqrt(128)
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, scale, causal)
+    o, lse = _run_paged(api, inp, splits, causal)
+    e = max_err(o, ref_o)
+    el = lse_err(lse, ref_lse)
+    say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_paged_d64(api):
+    inp = _paged((7, 70, 300), 5, D=64, seed=3)
+    ref_o, _ = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                      inp.seq_lens, 0.125, True)
+    o, _ = _run_paged(api, inp, 2, True, 0.125)
+    assert max_err(o, ref_o) <= TOL_BF16
+
+
+@pytest.mark.parametrize("splits", [1, 16])
+def test_paged_bit_identical_under_block_permutation(api, splits):
+    inp = _paged((5, 100, 257, 1000), 5, seed=9)
+    o1, l1 = _run_paged(api, inp, splits)
+    perm = permute_pool(inp, 1234)
+    assert not torch.equal(perm.block_tables, inp.block_tables)
+    o2, l2 = _run_paged(api, perm, splits)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_split_invariance(api):
+    inp = _paged((2000, 3000, 4096), 5, seed=10)
+    o1, _ = _run_paged(api, inp, 1)
+    for s in [2, 7, 16, 64]:
+        o2, _ = _run_paged(api, inp, s)
+        d = (o1.float() - o2.float()).abs().max().item()
+        say(f"  S=1 vs S={s}: {d:.3e}")
+        assert d <= TOL_BF16
+
+
+def test_paged_full_query_matches_prefill(api):
+    """q_len == seq_len over a fresh paged sequence equals causal prefill."""
+    n = 16
+    inp = _paged((n,), n, H=2, seed=4, poison=False)
+    kc = oracle.paged_gather(inp.k_pool, inp.block_tables, inp.seq_lens)[0][None]
+    vc = oracle.paged_gather(inp.v_pool, inp.block_tables, inp.seq_lens)[0][None]
+    o_paged, _ = _run_paged(api, inp, 1)
+    o_pre = api.attn_prefill(*to_dev(inp.q, kc, vc), causal=True)
+    d = (o_paged.float() - o_pre.float()).abs().max().item()
+    say(f"  paged vs prefill: {d:.3e}")
+    assert d <= TOL_BF16
+
+
+def test_paged_shared_prefix(api):
+    inp = _paged((40, 64, 90, 33), 5, seed=12, prefix=2)
+    ref_o, _ = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                      inp.seq_lens, 1 / math.sqrt(128), True)
+    o, _ = _run_paged(api, inp, 3)
+    assert max_err(o, ref_o) <= TOL_BF16
+
+
+# ------------------------------------------------------------------- gather ---
+
+def test_gather_bit_exact(api):
+    inp = _paged((1, 16, 17, 100, 257), 1, seed=2, extra=6)
+    ml = 300
+    out = api.attn_paged_gather(*to_dev(inp.k_pool, inp.block_tables, inp.seq_lens), ml)
+    ref = oracle.paged_gather(inp.k_pool, inp.block_tables, inp.seq_lens)
+    got = out.cpu()
+    for b, n in enumerate(inp.seq_lens.tolist()):
+        assert torch.equal(got[b, :, :n].view(torch.int16), ref[b].view(torch.int16))
+        assert torch.all(got[b, :, n:] == 0)
+
+
+def test_gather_paging_figure(api):
+    """The pool of the paging figure in [P1] section 3.2, A:[0,1,5,7,8], B:[2,9]."""
+    H, D = 2, 64
+    pool = torch.arange(11 * H * 16 * D, dtype=torch.float32).reshape(11, H, 16, D)
+    pool = (pool % 251).to(torch.bfloat16)
+    tables = torch.tensor([[0, 1, 5, 7, 8], [2, 9, -1, -1, -1]], dtype=torch.int32)
+    lens = torch.tensor([70, 20], dtype=torch.int32)
+    out = api.attn_paged_gather(*to_dev(pool, tables, lens), 80).cpu()
+    ref = oracle.paged_gather(pool, tables, lens)
+    assert torch.equal(out[0, :, :70], ref[0]) and torch.equal(out[1, :, :20], ref[1])
+
+
+# -------------------------------------------------------------------- merge ---
+
+@pytest.mark.parametrize("S", [1, 3, 16])
+def test_lse_merge(api, S):
+    g = torch.Generator().manual_seed(S)
+    B, H, ql, D = 2, 3, 5, 128
+    op = torch.randn(B, H, ql, S, D, generator=g)
+    lp = torch.randn(B, H, ql, S, generator=g) * 3
+    if S > 1:
+        lp[0, 0, 0, 1] = -float("inf")
+        lp[1, 2, 4, :] = -float("inf")
+    ref_o, ref_l = oracle.lse_merge(op.permute(3, 0, 1, 2, 4).numpy(), lp.permute(3, 0, 1, 2).numpy())
+    o32, l32 = api.attn_lse_merge(*to_dev(op, lp), out_dtype=torch.float32, return_lse=True)
+    obf = api.attn_lse_merge(*to_dev(op, lp), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert max_err(o32, ref_o) <= TOL_F32
+    assert max_err(obf, ref_o) <= TOL_BF16
+    assert lse_err(l32, ref_l) <= TOL_F32
+
+
+# ------------------------------------------------------ full-size paged ---
+
+@pytest.mark.parametrize("spec", [C4, C5], ids=["c4", "c5"])
+def test_paged_full_size_sampled(api, spec):
+    say(f"full-size {spec.name}")
+    inp = paged_inputs(spec)
+    lens = inp.seq_lens.tolist()
+    order = sorted(range(spec.B), key=lambda b: lens[b])
+    bs = sorted({order[0], order[-1], order[len(order) // 2], 1 % spec.B})
+    pairs = [(b, h) for b in bs for h in (0, spec.H - 1)]
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, spec.scale, spec.causal, heads=pairs)
+    o, lse = _run_paged(api, inp, spec.num_splits, spec.causal, spec.scale)
+    e = max_err(o, ref_o, pairs)
+    el = lse_err(lse, ref_lse, pairs)
+    say(f"  pairs={pairs} max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= TOL_BF16 and el <= TOL_LSE
+    # block-table indexing on the same pool, bit-exact, for the sampled sequences
+    ml = max(lens[b] for b in bs)
+    sel = torch.tensor(bs)
+    out = api.attn_paged_gather(inp.k_pool.cuda(), inp.block_tables[sel].cuda(),
+                                inp.seq_lens[sel].cuda(), ml).cpu()
+    ref = oracle.paged_gather(inp.k_pool, inp.block_tables[sel], inp.seq_lens[sel])
+    for i, b in enumerate(bs):
+        assert torch.equal(out[i, :, :lens[b]].view(torch.int16), ref[i].view(torch.int16))
