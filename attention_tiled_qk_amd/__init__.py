@@ -27,7 +27,7 @@ ATTN_BF16 = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it first (python -m attention_tiled_qk_amd.build "
+        f"{LIB_PATH} is missing: build it first (python attention_tiled_qk_amd/build.py "
         "or __graft_entry__.build()); there is no non-HIP implementation")
 
 lib = ctypes.CDLL(LIB_PATH)

@@ -3,24 +3,31 @@
 
 One step = one causal bf16 prefill of the 1.3B-model attention shape
 (B=8, H=16, L=1024, D=128) through ``attn_prefill``; ``value`` is its
-algorithmic TFLOP/s (4*D per visible query/key pair, causal pairs only),
-inputs resident in HBM before the timed region. The same run also times the
-paged-decode workloads (64 sequences x 40 heads, lengths U[128, 4096], q_len 1;
-and 4 x 40 heads, 32768 keys, q_len 5, 16 splits, shared 2048-token prefix)
-and reports their KV GB/s against the HBM peak under ``paged_decode``.
+algorithmic TFLOP/s (4*D FLOPs per visible query/key pair, causal pairs only)
+over the wall clock of the timed steps, inputs resident in HBM before the timed
+region. ``roofline`` prices the prefill kernel alone, its duration taken from
+HIP events recorded around each launch on the stream the library launches on
+(torch's current stream, which the binding passes down).
 
-Kernel durations come from HIP events recorded on the stream the kernels run
-on (torch's current stream, which the binding passes to the library). The
+The same run also measures, under ``secondary``:
+  * c3: causal bf16 prefill B=1, H=40, L=4096, D=128 (13B-style long prompt);
+  * c4: paged decode, 64 sequences x 40 heads, q_len 1, lengths U[128, 4096];
+  * c5: paged verify, 4 sequences x 40 heads, q_len 5, 32768 keys, shared
+    2048-token prefix, 16 splits merged by log-sum-exp;
+each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
-same workload on this host's cores.
+c2 workload on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+``--only NAME`` runs a single workload (c2, c3, c4, c5, or ``copy``: a plain
+device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
+its entry; that is the form the profiler runs use.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
 """
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -28,6 +35,7 @@ import time
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak, GB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "prefill attn TFLOP/s (%MFMA peak); paged-decode KV GB/s (%HBM peak)"
 
 
 def log(msg):
@@ -39,16 +47,6 @@ def prefill_flops(B, H, L, D, causal):
     return 4.0 * D * pairs * B * H
 
 
-def prefill_bytes(B, H, L, D, elem=2):
-    return 4.0 * B * H * L * D * elem  # read Q, K, V once, write O once
-
-
-def paged_bytes(lens, H, D, q_len, elem=2):
-    kv = 2.0 * H * D * elem * sum(lens)
-    qo = 2.0 * len(lens) * H * q_len * D * elem
-    return kv, kv + qo
-
-
 def source_digest(*names):
     h = hashlib.sha256()
     for n in names:
@@ -57,27 +55,34 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key, digest, algo_bytes):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+KERNEL_SOURCES = {
+    "prefill": ("prefill_bf16.hip", "common.h"),
+    "paged": ("paged.hip", "common.h"),
+}
+
+
+def load_traffic(key, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(kernel_key)
+    ent = data.get(key)
     if not ent or ent.get("source_digest") != digest:
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
 def time_launches(torch, fn, warmup, steps):
-    """Average duration (ms) of fn() over `steps` launches, HIP events per launch."""
+    """Per-launch HIP-event durations (ms) and the wall time (ms) of `steps` calls."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
@@ -86,12 +91,11 @@ def time_launches(torch, fn, warmup, steps):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return sum(per) / len(per), wall, per
+    return per, wall
 
 
 def cpu_baseline(spec, budget_s):
     """Time the oracle on as many heads of `spec` as fit in about budget_s."""
-    import numpy as np
     import oracle
     from workloads import prefill_inputs
     try:
@@ -111,19 +115,56 @@ def cpu_baseline(spec, budget_s):
     dt = time.perf_counter() - t0
     flops = prefill_flops(1, done, spec.L, spec.D, spec.causal)
     cores = len(os.sched_getaffinity(0))
-    del np
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": blas_threads if blas_threads else cores,
         "host_cores": cores,
         "kind": "oracle",
-        "sample": f"{done} of {len(pairs)} (batch, head) pairs of the same workload, float64, "
+        "sample": f"{done} of {len(pairs)} (batch, head) pairs of the c2 workload, float64, "
                   f"{dt:.1f} s wall; rate counts the same algorithmic (causal) FLOPs as the GPU",
     }
 
 
-def bench_decode(torch, api, spec, warmup, steps):
+def bench_prefill(torch, api, spec, warmup, steps, key):
+    from workloads import prefill_inputs
+    log(f"[bench] building {spec.name} inputs")
+    q, k, v = (t.cuda() for t in prefill_inputs(spec))
+    o = torch.empty_like(q)
+
+    def call():
+        api.attn_prefill(q, k, v, causal=spec.causal, scale=spec.scale, o=o)
+
+    per, wall = time_launches(torch, call, warmup, steps)
+    kernel_ms = sum(per) / len(per)
+    flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = load_traffic(key, source_digest(*KERNEL_SOURCES["prefill"]))
+    log(f"[bench] {spec.name}: {kernel_ms * 1e3:.1f} us/launch (events), "
+        f"{wall / steps * 1e3:.1f} us/step (wall), {achieved:.0f} TFLOP/s "
+        f"({achieved / PEAK_BF16_TFLOPS:.1%} of peak)")
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return {
+        "workload": spec.name,
+        "ms_per_step": wall / steps,
+        "value": flops / (wall / steps * 1e-3) / 1e12,
+        "roofline": {
+            "kernel": f"prefill_bf16_kernel<{spec.D}, causal={int(spec.causal)}>",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": flops,
+            "launch_us_events": kernel_ms * 1e3,
+            "launch_us_min": min(per) * 1e3,
+        },
+    }
+
+
+def bench_paged(torch, api, spec, warmup, steps, key):
     from workloads import paged_inputs
     log(f"[bench] building {spec.name} inputs")
     inp = paged_inputs(spec)
@@ -135,33 +176,54 @@ def bench_decode(torch, api, spec, warmup, steps):
     ws_bytes = api.attn_paged_workspace_bytes(B, H, q_len, D, width, spec.num_splits)
     ws = torch.empty(max(ws_bytes // 4, 1), device="cuda", dtype=torch.float32)
     o = torch.empty_like(dq)
-    splits = spec.num_splits
 
     def call():
         api.attn_paged_decode(dq, dk, dv, dt, dl, causal=spec.causal, scale=spec.scale,
-                              num_splits=splits, o=o, workspace=ws)
+                              num_splits=spec.num_splits, o=o, workspace=ws)
 
-    ms, wall, _ = time_launches(torch, call, warmup, steps)
-    kv, total = paged_bytes(lens, H, D, q_len)
-    unique_kv = kv
-    if spec.shared_prefix_blocks:
-        shared_tokens = spec.shared_prefix_blocks * 16
-        unique_kv = kv - (B - 1) * 2.0 * H * D * 2 * shared_tokens
+    per, wall = time_launches(torch, call, warmup, steps)
+    ms = sum(per) / len(per)
+    # K and V bytes of every visible token, as the sequences address them
+    kv = 2.0 * H * D * 2 * sum(lens)
+    # bytes that must come from HBM: the shared prefix blocks are read once
+    unique_kv = kv - (B - 1) * 2.0 * H * D * 2 * spec.shared_prefix_blocks * 16
+    gbs = unique_kv / (ms * 1e-3) / 1e9
+    traffic = load_traffic(key, source_digest(*KERNEL_SOURCES["paged"]))
+    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})")
     res = {
         "workload": spec.name,
-        "num_splits": splits if splits else "auto",
-        "ms_per_call": ms,
-        "kv_bytes": kv,
-        "kv_GBps": kv / (ms * 1e-3) / 1e9,
-        "frac_hbm_peak": kv / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "num_splits": spec.num_splits if spec.num_splits else "auto",
+        "ms_per_step": wall / steps,
+        "value": unique_kv / (wall / steps * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "paged_attn_kernel<128> (+ lse_merge_kernel when split)",
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": unique_kv,
+            "logical_kv_bytes": kv,
+            "launch_us_events": ms * 1e3,
+            "launch_us_min": min(per) * 1e3,
+        },
     }
-    if spec.shared_prefix_blocks:
-        res["unique_kv_bytes"] = unique_kv
-        res["unique_kv_GBps"] = unique_kv / (ms * 1e-3) / 1e9
-    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/call, {res['kv_GBps']:.0f} GB/s")
     del dq, dk, dv, dt, dl, ws, o
     torch.cuda.empty_cache()
     return res
+
+
+def bench_copy(torch, warmup, steps):
+    """Plain 2 GiB device copy: the calibration kernel for HBM byte counters."""
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    per, wall = time_launches(torch, lambda: dst.copy_(src), warmup, steps)
+    ms = sum(per) / len(per)
+    log(f"[bench] copy 2 GiB: {ms * 1e3:.1f} us, {2 * n / (ms * 1e-3) / 1e9:.0f} GB/s (read+write)")
+    return {"workload": "copy_2GiB", "bytes_read": n, "bytes_written": n,
+            "ms_per_step": wall / steps, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}
 
 
 def main():
@@ -171,7 +233,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--no-decode", action="store_true", help="skip the paged-decode workloads")
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "copy"],
+                    help="run one workload and print its entry only")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -182,90 +245,49 @@ def main():
         sys.exit(2)
 
     import torch
-    import attention_tiled_qk_amd as api
-    from workloads import C2, C4, C5, prefill_inputs
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    import attention_tiled_qk_amd as api
+    from workloads import C2, C3, C4, C5
 
-    spec = C2
-    log(f"[bench] building {spec.name} inputs")
-    q, k, v = (t.cuda() for t in prefill_inputs(spec))
-    o = torch.empty_like(q)
+    steps, warmup = args.steps, args.warmup
+    runners = {
+        "c2": lambda: bench_prefill(torch, api, C2, warmup, steps, "prefill_c2"),
+        "c3": lambda: bench_prefill(torch, api, C3, warmup, max(steps // 2, 3), "prefill_c3"),
+        "c4": lambda: bench_paged(torch, api, C4, warmup, max(steps // 2, 3), "paged_c4"),
+        "c5": lambda: bench_paged(torch, api, C5, warmup, max(steps // 2, 3), "paged_c5"),
+        "copy": lambda: bench_copy(torch, warmup, steps),
+    }
+    if args.only:
+        print(json.dumps({"only": args.only, **runners[args.only]()}), flush=True)
+        return
 
-    def step():
-        api.attn_prefill(q, k, v, causal=spec.causal, scale=spec.scale, o=o)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record()
-        step()
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
-    ms_per_step = wall_ms / args.steps
-
-    flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    digest = source_digest("prefill_bf16.hip", "common.h")
-    traffic = load_traffic("prefill_bf16_c2", digest, prefill_bytes(spec.B, spec.H, spec.L, spec.D))
-    log(f"[bench] {spec.name}: {kernel_ms * 1e3:.1f} us/launch (events), "
-        f"{ms_per_step * 1e3:.1f} us/step (wall), {achieved:.0f} TFLOP/s")
-
+    main_res = runners["c2"]()
     out = {
-        "metric": "prefill attn TFLOP/s (%MFMA peak); paged-decode KV GB/s (%HBM peak)",
-        "value": value,
+        "metric": METRIC,
+        "value": main_res["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "causal prefill bf16 B=8 H=16 L=1024 D=128 (1.3B-model attention shape)",
-                   "B": spec.B, "H": spec.H, "L": spec.L, "D": spec.D, "causal": spec.causal,
-                   "seed": spec.seed},
-        "roofline": {
-            "kernel": "prefill_bf16_kernel<128,4,causal>",
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
-            "algorithmic_flops_per_launch": flops,
-            "launch_ms_events": kernel_ms,
-        },
+                   "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
+                   "seed": C2.seed},
+        "roofline": main_res["roofline"],
+        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5")},
     }
-    del q, k, v, o
-    torch.cuda.empty_cache()
-
-    if not args.no_decode:
-        decode = {}
-        for s in (C4, C5):
-            decode[s.name[:2]] = bench_decode(torch, api, s, args.warmup, max(args.steps // 2, 5))
-        decode["bound"] = "hbm"
-        decode["peak_GBps"] = PEAK_HBM_GBS
-        out["paged_decode"] = decode
-
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(C2, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
-
     print(json.dumps(out), flush=True)
 
 
