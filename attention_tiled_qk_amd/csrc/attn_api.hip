@@ -100,6 +100,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
   if (lse && !aligned4(lse)) return ATTN_ERR_MISALIGNED;
   if (checked_mul({B, H, L, D, 4}) < 0) return ATTN_ERR_OVERFLOW;
+  // the bf16 kernel addresses one head's K/V through a 32-bit byte range
+  if ((long long)L * D * 2 > 0x7fffffffLL) return ATTN_ERR_OVERFLOW;
   const int rows = dtype == ATTN_BF16 ? kPrefillRowsBf16 : kPrefillRowsF32;
   if ((long long)B * H * ((L + rows - 1) / rows) > kMaxGrid) return ATTN_ERR_OVERFLOW;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

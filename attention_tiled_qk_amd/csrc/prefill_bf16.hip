@@ -3,241 +3,319 @@
 // What is computed: O = softmax(scale * Q K^T + mask) V per (batch, head)
 // ([P2] §一), by the tiled online-softmax method of [P1] §2.2: Q is cut into
 // row tiles (one workgroup each, the query-sequence parallelism that the
-// FlashAttention-2 item of [P3] adds), K/V into 64-key tiles streamed through
-// LDS; every row keeps a running max m and exp-sum l, the output accumulator is
-// rescaled only when m grows, and O is divided by l once after the last tile.
-// Nothing of size L x L is ever written to memory.
+// FlashAttention-2 item of [P3] adds), K/V into BN-key tiles streamed through
+// LDS; every row keeps a running max m and exp-sum l, and O is divided by l
+// once after the last tile. Nothing of size L x L is ever written to memory.
 //
 // gfx950 mapping (per workgroup of NW waves, BM = 32 * NW query rows):
+//   * K/V tiles move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
+//     register round trip) into ST rotating stages, so tile j+ST-1 is in flight
+//     while tile j is consumed; one barrier per tile. The buffer descriptor of
+//     each tile ends at the head's last key, so rows past L arrive as zeros.
+//   * LDS tiles are unpadded; 16-byte chunks are XOR-swizzled per row (a
+//     different swizzle for K and for V) so that the K operand reads and the
+//     transposing V reads below are free of bank conflicts. The swizzle is
+//     applied on the load side by choosing which global chunk each lane fetches.
 //   * each wave owns 32 query rows; Q stays in VGPRs as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane's accumulators hold
-//     16 keys of ONE query: the row max / row sum is an in-lane reduction plus
-//     one permlane32 swap, and the output accumulator O^T keeps one query per
-//     lane too, so its rescale is a broadcast multiply;
+//     keys of ONE query: the row max / row sum are in-lane reductions plus one
+//     permlane32 swap, and the O^T accumulator keeps one query per lane too;
 //   * P^T feeds O^T += V^T P^T straight from the S^T accumulators (converted to
-//     bf16 in registers, no LDS round trip); V^T operands come from the
-//     row-major V tile in LDS through ds_read_b64_tr_b16 transposing reads;
-//   * K/V tiles are double-buffered in LDS with padded row pitches chosen so
-//     the 16-byte K reads and the transposing V reads are free of bank conflicts;
+//     bf16 in registers); V^T operands come from the row-major V tile through
+//     ds_read_b64_tr_b16 transposing reads;
+//   * the running max is only moved when a row's maximum grows by more than
+//     2^8 in exp2 units. Any reference value m gives the same O = sum(e^(s-m) v)
+//     / sum(e^(s-m)); keeping a stale m bounds P by 2^8 and skips the rescale of
+//     the accumulators on almost every tile;
 //   * causal: key tiles above a wave's last row are skipped, the mask is only
 //     evaluated on tiles that cross the diagonal, workgroups are ordered
 //     heavy-first within a head and heads are kept on one XCD (xcd_remap).
+#include <type_traits>
+
 #include "common.h"
 
 namespace attn {
 
 namespace {
 
-constexpr int BN = 64;  // keys per tile
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw (unformatted) buffer descriptor, gfx9
+constexpr float kRescaleLog2 = 8.f;           // move m only when P could exceed 2^8
 
-template <int D, int NW>
+// Buffer descriptor over [base, base + bytes): reads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane (lds uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, ATTN_LDS void* lds, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+// Workgroup barrier that orders LDS accesses only (outstanding global loads,
+// i.e. the prefetch of later tiles, are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, int NW, int BN, int ST>
 struct PrefillCfg {
-  static constexpr int BM = 32 * NW;
-  static constexpr int KC = D / 16;          // 16-wide k chunks of the QK^T contraction
-  static constexpr int DB = D / 32;          // 32-wide output column blocks
-  static constexpr int PK = D * 2 + 16;      // K tile row pitch (bytes)
-  static constexpr int PV = D * 2 + 64;      // V tile row pitch (bytes)
-  static constexpr int K_BYTES = BN * PK;
-  static constexpr int V_BYTES = BN * PV;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int BM = 32 * NW;        // query rows per workgroup
+  static constexpr int KC = D / 16;         // 16-wide k chunks of the QK^T contraction
+  static constexpr int DB = D / 32;         // 32-wide output column blocks
+  static constexpr int NCH = D / 8;         // 16-byte chunks per K/V row
+  static constexpr int ROWB = 2 * D;        // bytes per K/V row
+  static constexpr int TILEB = BN * ROWB;   // bytes per K (or V) tile
+  static constexpr int PIECES = TILEB / 1024;
+  static constexpr int PPW = PIECES / NW;   // 1 KB pieces per wave per tile (K or V)
+  static constexpr int RPP = 1024 / ROWB;   // rows per piece
+  static constexpr int NKB = BN / 32;       // 32-key blocks per tile
+  static constexpr int LOADS = 2 * PPW;     // buffer loads per wave per tile
   static constexpr int THREADS = NW * 64;
-  static constexpr int CHUNKS = BN * D / 8;  // 16-byte chunks per K (or V) tile
-  static constexpr int CPT = CHUNKS / THREADS;
-  static_assert(CHUNKS % THREADS == 0, "tile chunks must divide evenly");
+  static_assert(PIECES % NW == 0 && PPW >= 1, "tile pieces must split evenly over the waves");
+  static_assert(ST == 2 || ST == 3, "two or three LDS stages");
+  static_assert(BN % 32 == 0, "key tile is a multiple of 32");
 };
+
+// Swizzle of the 16-byte chunk index within a K row: chunk c of row r is stored
+// at c ^ kswz(r). Sixteen consecutive rows (one 16-lane group of the K operand
+// read) then cover all 64 banks: at D = 128 a row is one bank sweep and the
+// chunk moves with r; at D = 64 two rows share a sweep and it moves with r / 2.
+template <int NCH>
+__device__ __forceinline__ int kswz(int r) { return (NCH == 16 ? r : r >> 1) & (NCH - 1); }
+// V rows: the transposing read touches 8 consecutive rows x 4 chunks; rows
+// r & 3 go to different 64-byte groups and (r >> 2) & 1 permutes within them.
+template <int NCH>
+__device__ __forceinline__ int vswz(int r) { return (((r & 3) << 2) | ((r >> 2) & 1)) & (NCH - 1); }
 
 }  // namespace
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int BN, int ST, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int BH, int L, int n_qtiles, float scale) {
-  using C = PrefillCfg<D, NW>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  ATTN_LDS unsigned char* smem = (ATTN_LDS unsigned char*)smem_raw;
+    bf16* __restrict__ o, float* __restrict__ lse, int L, int n_qtiles, float scale) {
+  using C = PrefillCfg<D, NW, BN, ST>;
+  // one object per stage, so the compiler can tell the stages' LDS-DMA writes apart
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks2[ST > 2 ? C::TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs2[ST > 2 ? C::TILEB : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
-  const int g = lane >> 5;  // which half-wave (k group of the 32x32 operands)
+  const int g = lane >> 5;  // half-wave: k group of the 32x32 operands
 
   // ---- which (head, q-tile) this workgroup owns: head-major, heavy tiles first
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - id % n_qtiles) : (id % n_qtiles);
   const size_t head_off = (size_t)bh * L * D;
-  const bf16* qh = q + head_off;
   const bf16* kh = k + head_off;
   const bf16* vh = v + head_off;
 
-  const int q0 = qt * C::BM;               // first row of the workgroup
-  const int wrow0 = q0 + wave * 32;         // first row of this wave
-  const int my_row = wrow0 + l32;           // the query this lane accumulates
+  const int q0 = qt * C::BM;
+  const int wrow0 = q0 + wave * 32;
+  const int my_row = wrow0 + l32;
 
-  // ---- Q operand in registers: lane holds d = 16 kc + 8 g + (0..7) of my_row
+  const int n_kt = CAUSAL ? (min(q0 + C::BM, L) - 1) / BN + 1 : (L + BN - 1) / BN;
+
+  // ---- per-lane offsets of the loads into LDS (fixed across tiles)
+  unsigned koff[C::PPW], voff[C::PPW];
+#pragma unroll
+  for (int i = 0; i < C::PPW; ++i) {
+    const int piece = wave + NW * i;
+    const int row = piece * C::RPP + lane / C::NCH;
+    const int phys = lane % C::NCH;
+    koff[i] = row * C::ROWB + (phys ^ kswz<C::NCH>(row)) * 16;
+    voff[i] = row * C::ROWB + (phys ^ vswz<C::NCH>(row)) * 16;
+  }
+  auto kst = [&](auto s) -> ATTN_LDS unsigned char* {
+    if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)ks0;
+    else if constexpr (decltype(s)::value == 1) return (ATTN_LDS unsigned char*)ks1;
+    else return (ATTN_LDS unsigned char*)ks2;
+  };
+  auto vst = [&](auto s) -> ATTN_LDS unsigned char* {
+    if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)vs0;
+    else if constexpr (decltype(s)::value == 1) return (ATTN_LDS unsigned char*)vs1;
+    else return (ATTN_LDS unsigned char*)vs2;
+  };
+  auto issue = [&](auto s, int kt) {
+    const int rows_left = L - kt * BN;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kh + (size_t)kt * BN * D, rows_left * C::ROWB);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vh + (size_t)kt * BN * D, rows_left * C::ROWB);
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) dma16(rk, kst(s) + (wave + NW * i) * 1024, koff[i]);
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) dma16(rv, vst(s) + (wave + NW * i) * 1024, voff[i]);
+  };
+
+  // ---- per-lane LDS read offsets (fixed across tiles and stages)
+  // K operand, chunk kc: row l32 (+32 per key block), logical chunk 2 kc + g
+  int kaddr[C::KC];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc)
+    kaddr[kc] = l32 * C::ROWB + (((2 * kc + g) ^ kswz<C::NCH>(l32)) * 16);
+  // V^T operand, column block db: the transposing read of lane (grp, i16)
+  // addresses row 4 g + i16/4 (+16 per 16-key chunk, +8 for the second half)
+  // and columns db*32 + 16 (grp & 1) + 4 (i16 & 3) .. +3
+  int vaddr[C::DB];
+  {
+    const int i16 = lane & 15;
+    const int grp = lane >> 4;
+    const int r = 4 * g + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int c = db * 4 + 2 * (grp & 1) + ((i16 & 3) >> 1);
+      vaddr[db] = r * C::ROWB + ((c ^ vswz<C::NCH>(r)) * 16) + 8 * (i16 & 1);
+    }
+  }
+
+  // ---- Q (B operand: lane holds d = 16 kc + 8 g + 0..7). A negative scale is
+  // folded into Q (exact sign flip) so the running max is always taken over
+  // scores that the exponent multiplies by a positive factor.
+  const bool neg = scale < 0.f;
+  const float sc_abs = neg ? -scale : scale;
   bf16x8 qreg[C::KC];
   {
     const bool ok = my_row < L;
-    const u32x4* src = reinterpret_cast<const u32x4*>(qh + (size_t)(ok ? my_row : 0) * D + 8 * g);
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + head_off + (size_t)(ok ? my_row : 0) * D + 8 * g);
+    const unsigned flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
       u32x4 w = ok ? src[kc * 2] : u32x4{0, 0, 0, 0};
+      w ^= flip;
       qreg[kc] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  // ---- key tiles this workgroup visits
-  const int n_ktiles_all = (L + BN - 1) / BN;
-  const int n_kt = CAUSAL ? min(n_ktiles_all, (min(q0 + C::BM, L) - 1) / BN + 1) : n_ktiles_all;
+  // ---- start streaming K/V (after Q, so the in-order load counter covers Q first)
+  issue(std::integral_constant<int, 0>{}, 0);
+  if constexpr (ST == 3) {
+    if (n_kt > 1) issue(std::integral_constant<int, 1>{}, 1);
+  }
 
-  // global -> register staging of one K and one V tile (rows past L become 0)
-  u32x4 kst[C::CPT], vst[C::CPT];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ci = tid + i * C::THREADS;
-      const int r = ci / (D / 8);
-      const int cc = ci % (D / 8);
-      const int key = kt * BN + r;
-      if (key < L) {
-        const size_t off = (size_t)key * D + cc * 8;
-        kst[i] = *reinterpret_cast<const u32x4*>(kh + off);
-        vst[i] = *reinterpret_cast<const u32x4*>(vh + off);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    ATTN_LDS unsigned char* base = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ci = tid + i * C::THREADS;
-      const int r = ci / (D / 8);
-      const int cc = ci % (D / 8);
-      *reinterpret_cast<ATTN_LDS u32x4*>(base + r * C::PK + cc * 16) = kst[i];
-      *reinterpret_cast<ATTN_LDS u32x4*>(base + C::K_BYTES + r * C::PV + cc * 16) = vst[i];
-    }
-  };
-
-  // ---- running softmax state of my_row (raw-score units) and O^T accumulators
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // raw-score units
   float l_run = 0.f;
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  const float c = sc_abs * kLog2e;  // exp(scale*(s-m)) == 2^(c*(s-m))
 
-  const float c = scale * kLog2e;  // exp(scale*(s-m)) == 2^(c*(s-m))
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-
+  auto compute = [&](auto s, int kt) {
     const int key0 = kt * BN;
-    // a wave whose rows all precede this tile has nothing to do in it
-    const bool active = !CAUSAL || key0 <= wrow0 + 31;
-    if (active) {
-      const ATTN_LDS unsigned char* kb_base = smem + buf * C::STAGE;
-      const ATTN_LDS unsigned char* vb_base = kb_base + C::K_BYTES;
+    if (CAUSAL && key0 > wrow0 + 31) return;  // every row of this wave precedes the tile
+    const ATTN_LDS unsigned char* kb_ = kst(s);
+    const ATTN_LDS unsigned char* vb_ = vst(s);
 
-      // S^T[key][query] for two 32-key blocks
-      f32x16 s[2];
+    f32x16 sc[C::NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const ATTN_LDS unsigned char* row = kb_base + (kb * 32 + l32) * C::PK + g * 16;
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      sc[kb] = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < C::KC; ++kc) {
-          bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(row + kc * 32);
-          s[kb] = mfma32(a, qreg[kc], s[kb]);
-        }
-      }
-
-      // mask only where the tile reaches past the wave's first row or past L
-      const bool need_mask = (CAUSAL && key0 + BN - 1 > wrow0) || (key0 + BN > L);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = key0 + kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            const bool vis = (key < L) && (!CAUSAL || key <= my_row);
-            s[kb][j] = vis ? s[kb][j] : -INFINITY;
-          }
-      }
-
-      // row max over this tile: 32 in-lane values, then the other half-wave
-      float mt = s[0][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mt = fmaxf(mt, s[0][j]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[1][j]);
-      mt = max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-
-      // rescale l and O only when some row's max grew (wave-uniform branch)
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        // m_run = -inf gives 0; rows whose max did not move keep alpha = 1
-        const float alpha = m_new == m_run ? 1.f : exp2_fast((m_run - m_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = (m_run == -INFINITY ? 0.f : m_run) * c;
-
-      // P = 2^(c s - c m); pack into the bf16 B operands of O^T += V^T P^T
-      bf16x8 p[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e[i] = exp2_fast(__builtin_fmaf(s[kb][8 * h + i], c, -mc));
-            lsum += e[i];
-          }
-          u32x4 w;
-          w[0] = pack_bf16x2(e[0], e[1]);
-          w[1] = pack_bf16x2(e[2], e[3]);
-          w[2] = pack_bf16x2(e[4], e[5]);
-          w[3] = pack_bf16x2(e[6], e[7]);
-          p[kb * 2 + h] = __builtin_bit_cast(bf16x8, w);
-        }
-      l_run += lsum;
-
-      // O^T[d][query] += V^T P^T. Chunk cidx covers keys 16 cidx .. +15; this
-      // lane's P elements 0..3 are keys 16 cidx + 4 g + (0..3) and elements 4..7
-      // are keys 16 cidx + 8 + 4 g + (0..3) (the S^T accumulator order), so the
-      // V^T operand is two transposing reads of 4 keys x 16 columns each.
-      const int i16 = lane & 15;
-      const int grp = lane >> 4;
-#pragma unroll
-      for (int cidx = 0; cidx < 4; ++cidx) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int col = db * 32 + (grp & 1) * 16 + 4 * (i16 & 3);
-          const int r0 = cidx * 16 + 4 * g + (i16 >> 2);
-          const ATTN_LDS bf16x4* a0 =
-              reinterpret_cast<const ATTN_LDS bf16x4*>(vb_base + r0 * C::PV + col * 2);
-          const ATTN_LDS bf16x4* a1 =
-              reinterpret_cast<const ATTN_LDS bf16x4*>(vb_base + (r0 + 8) * C::PV + col * 2);
-          bf16x8 a = join(lds_read_tr(a0), lds_read_tr(a1));
-          acc[db] = mfma32(a, p[cidx], acc[db]);
-        }
+      for (int kc = 0; kc < C::KC; ++kc) {
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kb_ + kaddr[kc] + kb * 32 * C::ROWB);
+        sc[kb] = mfma32(a, qreg[kc], sc[kb]);
       }
     }
 
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+    // mask where the tile reaches past the wave's first row (causal) or past L
+    const bool need_mask = CAUSAL ? (key0 + BN - 1 > wrow0) : (key0 + BN > L);
+    if (need_mask) {
+      // key of sc[kb][j] is key0 + kb*32 + 8 (j/4) + 4 g + j%4
+      const int lim = (CAUSAL ? my_row : L - 1) - key0 - 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          sc[kb][j] = (kb * 32 + 8 * (j >> 2) + (j & 3) <= lim) ? sc[kb][j] : -INFINITY;
+    }
+
+    float mt = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int j = (kb == 0 ? 1 : 0); j < 16; ++j) mt = fmaxf(mt, sc[kb][j]);
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    // NaN (both -inf: nothing visible yet) compares false and leaves m alone
+    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kRescaleLog2) != 0) {
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * c;
+
+    // P = 2^(c s - c m) as the bf16 B operands of O^T += V^T P^T
+    bf16x8 p[2 * C::NKB];
+    float part[2 * C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(sc[kb][8 * h + i], c, -mc));
+        part[2 * kb + h] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        u32x4 w;
+        w[0] = pack_bf16x2(e[0], e[1]);
+        w[1] = pack_bf16x2(e[2], e[3]);
+        w[2] = pack_bf16x2(e[4], e[5]);
+        w[3] = pack_bf16x2(e[6], e[7]);
+        p[2 * kb + h] = __builtin_bit_cast(bf16x8, w);
+      }
+    float lsum = part[0];
+#pragma unroll
+    for (int i = 1; i < 2 * C::NKB; ++i) lsum += part[i];
+    l_run += lsum;
+
+    // chunk cidx covers keys 16 cidx .. +15; this lane's P elements 0..3 are keys
+    // 16 cidx + 4 g + 0..3 and elements 4..7 are keys 16 cidx + 8 + 4 g + 0..3
+#pragma unroll
+    for (int cidx = 0; cidx < 2 * C::NKB; ++cidx) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const ATTN_LDS unsigned char* base = vb_ + vaddr[db] + cidx * 16 * C::ROWB;
+        const bf16x4 lo = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base));
+        const bf16x4 hi = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base + 8 * C::ROWB));
+        acc[db] = mfma32(join(lo, hi), p[cidx], acc[db]);
+      }
+    }
+  };
+
+  // stage S holds tile kt; on entry tiles kt .. kt+ST-2 may still be in flight
+  auto step = [&](auto s, int kt) {
+    constexpr int S = decltype(s)::value;
+    if constexpr (ST == 3) {
+      if (kt + 1 < n_kt) wait_vmcnt<C::LOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1's stage
+    if (kt + ST - 1 < n_kt) issue(std::integral_constant<int, (S + ST - 1) % ST>{}, kt + ST - 1);
+    compute(s, kt);
+  };
+
+  for (int kt = 0; kt < n_kt; kt += ST) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (ST == 3) {
+      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
+    }
   }
 
   // ---- epilogue: O = O / l, lse = scale * m + ln l
@@ -256,41 +334,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         *reinterpret_cast<u32x2*>(orow + d) = w;
       }
     if (lse != nullptr && g == 0)
-      lse[(size_t)bh * L + my_row] = l_tot > 0.f ? scale * m_run + __logf(l_tot) : -INFINITY;
+      lse[(size_t)bh * L + my_row] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
   }
 }
 
-template <int D, int NW, bool CAUSAL>
-static hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int B, int H, int L, float scale, hipStream_t stream) {
-  using C = PrefillCfg<D, NW>;
+template <int D, int NW, int BN, int ST, bool CAUSAL>
+hipError_t launch_prefill_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int B, int H, int L, float scale, hipStream_t stream) {
+  using C = PrefillCfg<D, NW, BN, ST>;
   const int n_qtiles = (L + C::BM - 1) / C::BM;
   const long long grid = (long long)B * H * n_qtiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const size_t shmem = 2 * C::STAGE;
-  auto kern = prefill_bf16_kernel<D, NW, CAUSAL>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), shmem, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, B * H, L,
-                     n_qtiles, scale);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BN, ST, CAUSAL>), dim3((unsigned)grid),
+                     dim3(C::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                     (bf16*)o, lse, L, n_qtiles, scale);
   return hipGetLastError();
 }
+
+// Query rows per workgroup of the configuration launch_prefill_bf16 uses.
+int prefill_bf16_rows() { return 128; }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int L, int D, int causal, float scale,
                                hipStream_t stream) {
   if (D == 128) {
-    return causal ? launch_one<128, 4, true>(q, k, v, o, lse, B, H, L, scale, stream)
-                  : launch_one<128, 4, false>(q, k, v, o, lse, B, H, L, scale, stream);
+    return causal ? launch_prefill_variant<128, 4, 64, 2, true>(q, k, v, o, lse, B, H, L, scale, stream)
+                  : launch_prefill_variant<128, 4, 64, 2, false>(q, k, v, o, lse, B, H, L, scale, stream);
   }
-  return causal ? launch_one<64, 4, true>(q, k, v, o, lse, B, H, L, scale, stream)
-                : launch_one<64, 4, false>(q, k, v, o, lse, B, H, L, scale, stream);
+  return causal ? launch_prefill_variant<64, 4, 64, 2, true>(q, k, v, o, lse, B, H, L, scale, stream)
+                : launch_prefill_variant<64, 4, 64, 2, false>(q, k, v, o, lse, B, H, L, scale, stream);
 }
 
 }  // namespace attn
