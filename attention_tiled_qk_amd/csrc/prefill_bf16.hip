@@ -40,6 +40,7 @@ namespace {
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw (unformatted) buffer descriptor, gfx9
 constexpr float kRescaleLog2 = 8.f;           // move m only when P could exceed 2^8
+constexpr float kMaxTileSum = 1073741824.f;   // 2^30: bound on one lane's P sum per tile
 
 // Buffer descriptor over [base, base + bytes): reads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
@@ -95,6 +96,23 @@ __device__ __forceinline__ int kswz(int r) { return (NCH == 16 ? r : r >> 1) & (
 // r & 3 go to different 64-byte groups and (r >> 2) & 1 permutes within them.
 template <int NCH>
 __device__ __forceinline__ int vswz(int r) { return (((r & 3) << 2) | ((r >> 2) & 1)) & (NCH - 1); }
+
+// Work item of workgroup `id`: (head bh, query tile qt). The dispatcher hands
+// workgroup ids to the 8 XCDs in turn (id % 8), each XCD starting them in id
+// order. When the head count splits evenly, XCD x owns a contiguous group of
+// heads (their K/V share its L2) and starts the longest causal tiles of all
+// its heads first, the shortest last, so the tail of the launch is short work.
+__device__ __forceinline__ void tile_of(int id, int n_heads, int n_qtiles, int& bh, int& qt) {
+  if ((n_heads & 7) == 0) {
+    const int hpx = n_heads >> 3;
+    const int pos = id >> 3;
+    qt = n_qtiles - 1 - pos / hpx;
+    bh = (id & 7) * hpx + pos % hpx;
+  } else {
+    qt = n_qtiles - 1 - id / n_heads;
+    bh = id % n_heads;
+  }
+}
 
 }  // namespace
 
@@ -338,6 +356,288 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Software-pipelined form of the same computation. Iteration j issues the
+// QK^T products of tile j+1 in the same instruction stream as the softmax of
+// tile j, so the matrix cores and the vector ALUs of one wave work at the same
+// time; then it accumulates P_j V_j. K and V have two LDS stages each: K_{j+2}
+// and V_{j+1} are loaded while K_{j+1} and V_j are read.
+template <int D, int NW, int BN, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_pipe_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, float* __restrict__ lse, int L, int n_heads, int n_qtiles, float scale) {
+  using C = PrefillCfg<D, NW, BN, 2>;
+  __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs1[C::TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  int bh, qt;
+  tile_of(blockIdx.x, n_heads, n_qtiles, bh, qt);
+  const size_t head_off = (size_t)bh * L * D;
+  const bf16* kh = k + head_off;
+  const bf16* vh = v + head_off;
+
+  const int q0 = qt * C::BM;
+  const int wrow0 = q0 + wave * 32;
+  const int my_row = wrow0 + l32;
+  const int n_kt = CAUSAL ? (min(q0 + C::BM, L) - 1) / BN + 1 : (L + BN - 1) / BN;
+  // last key tile holding a key that some row of this wave may see
+  const int last_w = CAUSAL ? min(n_kt - 1, (wrow0 + 31) / BN) : n_kt - 1;
+
+  unsigned koff[C::PPW], voff[C::PPW];
+#pragma unroll
+  for (int i = 0; i < C::PPW; ++i) {
+    const int piece = wave + NW * i;
+    const int row = piece * C::RPP + lane / C::NCH;
+    const int phys = lane % C::NCH;
+    koff[i] = row * C::ROWB + (phys ^ kswz<C::NCH>(row)) * 16;
+    voff[i] = row * C::ROWB + (phys ^ vswz<C::NCH>(row)) * 16;
+  }
+  auto kst = [&](auto s) -> ATTN_LDS unsigned char* {
+    if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)ks0;
+    else return (ATTN_LDS unsigned char*)ks1;
+  };
+  auto vst = [&](auto s) -> ATTN_LDS unsigned char* {
+    if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)vs0;
+    else return (ATTN_LDS unsigned char*)vs1;
+  };
+  auto issue_k = [&](auto s, int kt) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) dma16(r, kst(s) + (wave + NW * i) * 1024, koff[i]);
+  };
+  auto issue_v = [&](auto s, int kt) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
+#pragma unroll
+    for (int i = 0; i < C::PPW; ++i) dma16(r, vst(s) + (wave + NW * i) * 1024, voff[i]);
+  };
+
+  int kaddr[C::KC];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc)
+    kaddr[kc] = l32 * C::ROWB + (((2 * kc + g) ^ kswz<C::NCH>(l32)) * 16);
+  int vaddr[C::DB];
+  {
+    const int i16 = lane & 15;
+    const int grp = lane >> 4;
+    const int r = 4 * g + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int c = db * 4 + 2 * (grp & 1) + ((i16 & 3) >> 1);
+      vaddr[db] = r * C::ROWB + ((c ^ vswz<C::NCH>(r)) * 16) + 8 * (i16 & 1);
+    }
+  }
+
+  const bool neg = scale < 0.f;
+  const float sc_abs = neg ? -scale : scale;
+  bf16x8 qreg[C::KC];
+  {
+    const bool ok = my_row < L;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + head_off + (size_t)(ok ? my_row : 0) * D + 8 * g);
+    const unsigned flip = neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      u32x4 w = ok ? src[kc * 2] : u32x4{0, 0, 0, 0};
+      w ^= flip;
+      qreg[kc] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  issue_k(std::integral_constant<int, 0>{}, 0);
+  issue_v(std::integral_constant<int, 0>{}, 0);
+  if (n_kt > 1) issue_k(std::integral_constant<int, 1>{}, 1);
+
+  float m_run = -INFINITY;  // reference max (raw-score units)
+  float mc_run = 0.f;       // c * m_run, 0 while m_run is unset
+  float l_run = 0.f;
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  const float c = sc_abs * kLog2e;
+
+  auto qk = [&](f32x16* sc, const ATTN_LDS unsigned char* kb_) {
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      sc[kb] = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kb_ + kaddr[kc] + kb * 32 * C::ROWB);
+        sc[kb] = mfma32(a, qreg[kc], sc[kb]);
+      }
+    }
+  };
+  auto mask = [&](f32x16* sc, int kt) {
+    const int key0 = kt * BN;
+    const bool need_mask = CAUSAL ? (key0 + BN - 1 > wrow0) : (key0 + BN > L);
+    if (need_mask) {
+      const int lim = (CAUSAL ? my_row : L - 1) - key0 - 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          sc[kb][j] = (kb * 32 + 8 * (j >> 2) + (j & 3) <= lim) ? sc[kb][j] : -INFINITY;
+    }
+  };
+  // P = 2^(c s - mc) as the bf16 B operands of O^T += V^T P^T; returns this
+  // lane's sum of P over the tile
+  auto probs = [&](const f32x16* sc, bf16x8* p, float mc) -> float {
+    float part[2 * C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(sc[kb][8 * h + i], c, -mc));
+        part[2 * kb + h] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        u32x4 w;
+        w[0] = pack_bf16x2(e[0], e[1]);
+        w[1] = pack_bf16x2(e[2], e[3]);
+        w[2] = pack_bf16x2(e[4], e[5]);
+        w[3] = pack_bf16x2(e[6], e[7]);
+        p[2 * kb + h] = __builtin_bit_cast(bf16x8, w);
+      }
+    float lsum = part[0];
+#pragma unroll
+    for (int i = 1; i < 2 * C::NKB; ++i) lsum += part[i];
+    return lsum;
+  };
+  // Moves the reference max m to the running row maximum including this tile
+  // and returns the factor that l and O must be scaled by.
+  auto move_max = [&](const f32x16* sc) -> float {
+    float mt = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int j = (kb == 0 ? 1 : 0); j < 16; ++j) mt = fmaxf(mt, sc[kb][j]);
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    // m = -inf before gives 0; an unchanged m (also -inf == -inf) gives 1
+    const float alpha = m_new == m_run ? 1.f : exp2_fast((m_run - m_new) * c);
+    m_run = m_new;
+    mc_run = (m_run == -INFINITY ? 0.f : m_run) * c;
+    return alpha;
+  };
+  // Softmax of one tile into P. The exponents use the current reference m; only
+  // when some lane's P sum reaches 2^30 (scores grew by 30 / c past m, or m is
+  // still unset) is the row maximum taken, m moved and P recomputed. Any m gives
+  // the same O and l ratio, and P below 2^30 keeps l, O and the bf16 P finite.
+  auto softmax = [&](const f32x16* sc, bf16x8* p) {
+    float ls = probs(sc, p, mc_run);
+    if (__builtin_amdgcn_ballot_w64(!(ls < kMaxTileSum) || m_run == -INFINITY) != 0) {
+      const float alpha = move_max(sc);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      ls = probs(sc, p, mc_run);
+    }
+    l_run += ls;
+  };
+  auto pv = [&](const bf16x8* p, const ATTN_LDS unsigned char* vb_) {
+#pragma unroll
+    for (int cidx = 0; cidx < 2 * C::NKB; ++cidx) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const ATTN_LDS unsigned char* base = vb_ + vaddr[db] + cidx * 16 * C::ROWB;
+        const bf16x4 lo = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base));
+        const bf16x4 hi = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base + 8 * C::ROWB));
+        acc[db] = mfma32(join(lo, hi), p[cidx], acc[db]);
+      }
+    }
+  };
+
+  f32x16 sa[C::NKB], sb[C::NKB];
+  wait_vmcnt<0>();
+  lds_barrier();
+  qk(sa, kst(std::integral_constant<int, 0>{}));
+
+  // Iteration j (every wave takes part in its barrier and loads): tile j's
+  // scores are in s_cur, K_{j+1} and V_j are in LDS. The loop is split by
+  // wave-uniform phase -- tiles before the wave's last visible tile, that tile,
+  // and tiles past it -- so that the hot body has no branch between the
+  // products of tile j+1 and the softmax of tile j.
+  auto sync_and_load = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (j + 2 < n_kt) issue_k(std::integral_constant<int, P>{}, j + 2);
+    if (j + 1 < n_kt) issue_v(std::integral_constant<int, 1 - P>{}, j + 1);
+  };
+  auto full = [&](auto par, int j, f32x16* s_cur, f32x16* s_nxt) {
+    constexpr int P = decltype(par)::value;
+    sync_and_load(par, j);
+    mask(s_cur, j);
+    // products of tile j+1 and the softmax of tile j share one basic block
+    bf16x8 p[2 * C::NKB];
+    qk(s_nxt, kst(std::integral_constant<int, 1 - P>{}));
+    softmax(s_cur, p);
+    pv(p, vst(std::integral_constant<int, P>{}));
+  };
+  auto last = [&](auto par, int j, f32x16* s_cur) {
+    constexpr int P = decltype(par)::value;
+    sync_and_load(par, j);
+    mask(s_cur, j);
+    bf16x8 p[2 * C::NKB];
+    softmax(s_cur, p);
+    pv(p, vst(std::integral_constant<int, P>{}));
+  };
+
+  int j = 0;
+  for (; j + 1 < last_w; j += 2) {
+    full(std::integral_constant<int, 0>{}, j, sa, sb);
+    full(std::integral_constant<int, 1>{}, j + 1, sb, sa);
+  }
+  if (j < last_w) {
+    full(std::integral_constant<int, 0>{}, j, sa, sb);
+    last(std::integral_constant<int, 1>{}, j + 1, sb);
+    j += 2;
+  } else {
+    last(std::integral_constant<int, 0>{}, j, sa);
+    j += 1;
+  }
+  for (; j < n_kt; ++j) {
+    if (j & 1) sync_and_load(std::integral_constant<int, 1>{}, j);
+    else sync_and_load(std::integral_constant<int, 0>{}, j);
+  }
+
+  const float l_tot = sum_xor32(l_run);
+  if (my_row < L) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16* orow = o + head_off + (size_t)my_row * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = db * 32 + 8 * jj + 4 * g;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
+        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+    if (lse != nullptr && g == 0)
+      lse[(size_t)bh * L + my_row] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
+  }
+}
+
+template <int D, int NW, int BN, bool CAUSAL>
+hipError_t launch_prefill_pipe(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int L, float scale, hipStream_t stream) {
+  using C = PrefillCfg<D, NW, BN, 2>;
+  const int n_qtiles = (L + C::BM - 1) / C::BM;
+  const long long grid = (long long)B * H * n_qtiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_bf16_pipe_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)grid),
+                     dim3(C::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                     (bf16*)o, lse, L, B * H, n_qtiles, scale);
+  return hipGetLastError();
+}
+
 template <int D, int NW, int BN, int ST, bool CAUSAL>
 hipError_t launch_prefill_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                                   int B, int H, int L, float scale, hipStream_t stream) {
@@ -358,11 +658,11 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int B, int H, int L, int D, int causal, float scale,
                                hipStream_t stream) {
   if (D == 128) {
-    return causal ? launch_prefill_variant<128, 4, 64, 2, true>(q, k, v, o, lse, B, H, L, scale, stream)
-                  : launch_prefill_variant<128, 4, 64, 2, false>(q, k, v, o, lse, B, H, L, scale, stream);
+    return causal ? launch_prefill_pipe<128, 4, 64, true>(q, k, v, o, lse, B, H, L, scale, stream)
+                  : launch_prefill_pipe<128, 4, 64, false>(q, k, v, o, lse, B, H, L, scale, stream);
   }
-  return causal ? launch_prefill_variant<64, 4, 64, 2, true>(q, k, v, o, lse, B, H, L, scale, stream)
-                : launch_prefill_variant<64, 4, 64, 2, false>(q, k, v, o, lse, B, H, L, scale, stream);
+  return causal ? launch_prefill_pipe<64, 4, 64, true>(q, k, v, o, lse, B, H, L, scale, stream)
+                : launch_prefill_pipe<64, 4, 64, false>(q, k, v, o, lse, B, H, L, scale, stream);
 }
 
 }  // namespace attn
