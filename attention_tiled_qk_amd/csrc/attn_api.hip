@@ -47,15 +47,17 @@ long long checked_mul(std::initializer_list<long long> xs) {
   return r;
 }
 
-// Split count for paged decode when the caller leaves it to the library: enough
-// (split, head, sequence) waves to cover the chip several times over, but no
-// split shorter than 16 blocks (256 tokens) on the longest possible sequence.
+// Split count for paged decode when the caller leaves it to the library:
+// splits of about 32 blocks (512 tokens) on the longest possible sequence, so
+// that waves carry similar amounts of work whatever the length mix, raised
+// towards enough (split, head, sequence) waves to cover the chip several times
+// as long as every split keeps at least 4 blocks.
 int auto_splits(int B, int H, int max_blocks) {
+  long long s = (max_blocks + 31) / 32;
   const long long waves = (long long)B * H;
-  const long long want = (4096 + waves - 1) / waves;
-  long long cap = max_blocks / 16;
-  if (cap < 1) cap = 1;
-  long long s = want < cap ? want : cap;
+  long long fill = (2048 + waves - 1) / waves;
+  if (fill > max_blocks / 4) fill = max_blocks / 4;
+  if (s < fill) s = fill;
   if (s < 1) s = 1;
   if (s > ATTN_PAGED_MAX_SPLITS) s = ATTN_PAGED_MAX_SPLITS;
   return (int)s;

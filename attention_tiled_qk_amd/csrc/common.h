@@ -86,6 +86,33 @@ __device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw (unformatted) buffer descriptor, gfx9
+
+// Buffer descriptor over [base, base + bytes): reads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+// 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane (lds uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, ATTN_LDS void* lds, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+// Workgroup barrier that orders LDS accesses only (outstanding global loads,
+// i.e. the prefetch of later tiles, are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Workgroup id after an XCD-aware remap. The dispatcher hands consecutive
 // workgroup ids to the 8 XCDs in turn; this gives XCD x the contiguous logical
 // range [x * n / 8, (x + 1) * n / 8) so that workgroups sharing K/V (the tiles

@@ -26,6 +26,8 @@
 
 namespace attn {
 
+constexpr int kIdChunk = 256;  // block ids staged in LDS at a time (even)
+
 template <int D>
 __global__ __launch_bounds__(64) void paged_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_pool, const bf16* __restrict__ v_pool,
@@ -39,7 +41,9 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   constexpr int VCH = 16 * D / 8 / 64;  // 16-byte pieces of one slab per lane
   constexpr int CPR = D / 8;            // 16-byte pieces per slab row
   __shared__ __attribute__((aligned(16))) unsigned char vlds_raw[2 * 16 * PV];
+  __shared__ int ids_raw[kIdChunk];
   ATTN_LDS unsigned char* vlds = (ATTN_LDS unsigned char*)vlds_raw;
+  ATTN_LDS int* ids = (ATTN_LDS int*)ids_raw;
 
   const int lane = threadIdx.x;
   const int l16 = lane & 15;
@@ -101,44 +105,52 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float cs = scale * kLog2e;
 
-  for (int n = blk0; n < blk1; n += 2) {
-    const bool has_b = n + 1 < blk1;
-    const int pa = table[n];
-    const int pb = has_b ? table[n + 1] : pa;
-    const bf16* ka_src = k_pool + (size_t)pa * blk_stride + head_off;
-    const bf16* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
-    const bf16* va_src = v_pool + (size_t)pa * blk_stride + head_off;
-    const bf16* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
-
-    // K operands (row l16 of the slab) and V pieces (contiguous per instruction)
+  // K operands (row l16 of each slab) and V pieces (contiguous per instruction)
+  // of the block pair n, n+1. A missing second block reads as zeros.
+  struct Pair {
     bf16x8 ka[DC], kb[DC];
     u32x4 va[VCH], vb[VCH];
+  };
+  // the block ids of the current chunk [c0, c1) of this split sit in LDS;
+  // an id is read with a wave-uniform LDS load (no wait on global loads)
+  int c0 = blk0, c1 = blk0;
+  auto block_id = [&](int n) -> int { return __builtin_amdgcn_readfirstlane(ids[n - c0]); };
+  auto load = [&](int n, Pair& r) {
+    const bool has_b = n + 1 < c1;
+    const int pa = block_id(n);
+    const bf16* ka_src = k_pool + (size_t)pa * blk_stride + head_off;
+    const bf16* va_src = v_pool + (size_t)pa * blk_stride + head_off;
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-      ka[c] = *reinterpret_cast<const bf16x8*>(ka_src + l16 * D + 32 * c + 8 * g);
+      r.ka[c] = *reinterpret_cast<const bf16x8*>(ka_src + l16 * D + 32 * c + 8 * g);
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) va[i] = *reinterpret_cast<const u32x4*>(va_src + (i * 64 + lane) * 8);
+    for (int i = 0; i < VCH; ++i) r.va[i] = *reinterpret_cast<const u32x4*>(va_src + (i * 64 + lane) * 8);
     if (has_b) {
+      const int pb = block_id(n + 1);
+      const bf16* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
+      const bf16* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
 #pragma unroll
       for (int c = 0; c < DC; ++c)
-        kb[c] = *reinterpret_cast<const bf16x8*>(kb_src + l16 * D + 32 * c + 8 * g);
+        r.kb[c] = *reinterpret_cast<const bf16x8*>(kb_src + l16 * D + 32 * c + 8 * g);
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) vb[i] = *reinterpret_cast<const u32x4*>(vb_src + (i * 64 + lane) * 8);
+      for (int i = 0; i < VCH; ++i) r.vb[i] = *reinterpret_cast<const u32x4*>(vb_src + (i * 64 + lane) * 8);
     } else {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) kb[c] = bf16x8{};
+      for (int c = 0; c < DC; ++c) r.kb[c] = bf16x8{};
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) vb[i] = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < VCH; ++i) r.vb[i] = u32x4{0, 0, 0, 0};
     }
+  };
 
+  auto compute = [&](int n, Pair& r) {
     const int key0 = n * 16;
     const bool tail = key0 + 32 > key_end;
     if (tail) {  // V rows at or past the split's end must be exactly zero
 #pragma unroll
       for (int i = 0; i < VCH; ++i) {
         const int row = (i * 64 + lane) / CPR;
-        if (key0 + row >= key_end) va[i] = u32x4{0, 0, 0, 0};
-        if (key0 + 16 + row >= key_end) vb[i] = u32x4{0, 0, 0, 0};
+        if (key0 + row >= key_end) r.va[i] = u32x4{0, 0, 0, 0};
+        if (key0 + 16 + row >= key_end) r.vb[i] = u32x4{0, 0, 0, 0};
       }
     }
 
@@ -146,8 +158,8 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
     f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      sa = mfma16(ka[c], qreg[c], sa);
-      sb = mfma16(kb[c], qreg[c], sb);
+      sa = mfma16(r.ka[c], qreg[c], sa);
+      sb = mfma16(r.kb[c], qreg[c], sb);
     }
 
     if (tail || (causal && key0 + 31 > qpos0)) {
@@ -188,23 +200,43 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
     pw[3] = pack_bf16x2(e[6], e[7]);
     const bf16x8 p = __builtin_bit_cast(bf16x8, pw);
 
-    // V slabs -> LDS (row-major, padded rows), then transposing reads
-    __syncthreads();  // previous pair's reads are done before overwriting
+    // V slabs -> LDS (row-major, padded rows), then transposing reads. The
+    // workgroup is this one wave, whose LDS accesses execute in program order,
+    // so no barrier is needed (and none may wait for the next pair's loads).
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
       const int piece = i * 64 + lane;
       const int row = piece / CPR;
       const int col = piece % CPR;
-      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 16) = va[i];
-      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 16) = vb[i];
+      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 16) = r.va[i];
+      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 16) = r.vb[i];
     }
-    __syncthreads();
     const ATTN_LDS unsigned char* rd = vlds + (4 * g + (l16 >> 2)) * PV + 8 * (l16 & 3);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x4 lo = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(rd + db * 32));
       const bf16x4 hi = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(rd + 16 * PV + db * 32));
       acc[db] = mfma16(join(lo, hi), p, acc[db]);
+    }
+  };
+
+  // Chunks of up to kIdChunk blocks (an even number, so block pairs never
+  // straddle chunks). Within a chunk the loads are software-pipelined: the
+  // K/V of pair n+2 are in flight while pair n is computed.
+  for (; c0 < blk1; c0 = c1) {
+    c1 = min(c0 + kIdChunk, blk1);
+    for (int i = lane; i < c1 - c0; i += 64) ids[i] = table[c0 + i];
+    Pair r0, r1;
+    load(c0, r0);
+    for (int n = c0;;) {
+      if (n + 2 < c1) load(n + 2, r1);
+      compute(n, r0);
+      n += 2;
+      if (n >= c1) break;
+      if (n + 2 < c1) load(n + 2, r0);
+      compute(n, r1);
+      n += 2;
+      if (n >= c1) break;
     }
   }
 

@@ -38,34 +38,8 @@ namespace attn {
 
 namespace {
 
-constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw (unformatted) buffer descriptor, gfx9
 constexpr float kRescaleLog2 = 8.f;           // move m only when P could exceed 2^8
 constexpr float kMaxTileSum = 1073741824.f;   // 2^30: bound on one lane's P sum per tile
-
-// Buffer descriptor over [base, base + bytes): reads past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
-}
-
-// 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane (lds uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, ATTN_LDS void* lds, unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
-}
-
-// Wait until at most N vector-memory loads of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
-}
-
-// Workgroup barrier that orders LDS accesses only (outstanding global loads,
-// i.e. the prefetch of later tiles, are not waited for).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int D, int NW, int BN, int ST>
 struct PrefillCfg {

@@ -5,9 +5,10 @@ One step = one causal bf16 prefill of the 1.3B-model attention shape
 (B=8, H=16, L=1024, D=128) through ``attn_prefill``; ``value`` is its
 algorithmic TFLOP/s (4*D FLOPs per visible query/key pair, causal pairs only)
 over the wall clock of the timed steps, inputs resident in HBM before the timed
-region. ``roofline`` prices the prefill kernel alone, its duration taken from
-HIP events recorded around each launch on the stream the library launches on
-(torch's current stream, which the binding passes down).
+region. ``roofline`` prices the prefill kernel alone, its average duration
+taken from HIP events recorded around the timed back-to-back launches on the
+stream the library launches on (torch's current stream, which the binding
+passes down).
 
 The same run also measures, under ``secondary``:
   * c3: causal bf16 prefill B=1, H=40, L=4096, D=128 (13B-style long prompt);
@@ -76,22 +77,25 @@ def load_traffic(key, digest):
 
 
 def time_launches(torch, fn, warmup, steps):
-    """Per-launch HIP-event durations (ms) and the wall time (ms) of `steps` calls."""
+    """Average launch duration (ms) from HIP events recorded on the launch stream
+    around `steps` back-to-back calls, and the wall time (ms) of those calls.
+
+    Events bracket the whole run rather than each call: the host enqueues faster
+    than the kernels run, so the stream never idles between launches and the
+    event interval is the kernels' own time."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         fn()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return per, wall
+    return start.elapsed_time(end) / steps, wall
 
 
 def cpu_baseline(spec, budget_s):
@@ -135,7 +139,7 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
     api.attn_prefill(q, k, v, causal=spec.causal, scale=spec.scale, o=o)  # validates once
     # the same C-ABI call with its arguments marshalled once, so that the host
     # enqueues faster than the kernel runs and back-to-back launches keep the
-    # stream busy (per-launch events then time the kernel, not the host)
+    # stream busy
     P = ctypes.c_void_p
     args = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(o.data_ptr()), None,
             spec.B, spec.H, spec.L, spec.D, int(spec.causal), ctypes.c_float(spec.scale),
@@ -146,8 +150,7 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
         if fn(*args) != 0:
             raise RuntimeError("attn_prefill failed")
 
-    per, wall = time_launches(torch, call, warmup, steps)
-    kernel_ms = sum(per) / len(per)
+    kernel_ms, wall = time_launches(torch, call, warmup, steps)
     flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     traffic = load_traffic(key, source_digest(*KERNEL_SOURCES["prefill"]))
@@ -170,7 +173,6 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
             "traffic": traffic,
             "algorithmic_flops_per_launch": flops,
             "launch_us_events": kernel_ms * 1e3,
-            "launch_us_min": min(per) * 1e3,
         },
     }
 
@@ -202,8 +204,7 @@ def bench_paged(torch, api, spec, warmup, steps, key):
         if fn(*args) != 0:
             raise RuntimeError("attn_paged_decode failed")
 
-    per, wall = time_launches(torch, call, warmup, steps)
-    ms = sum(per) / len(per)
+    ms, wall = time_launches(torch, call, warmup, steps)
     # K and V bytes of every visible token, as the sequences address them
     kv = 2.0 * H * D * 2 * sum(lens)
     # bytes that must come from HBM: the shared prefix blocks are read once
@@ -227,7 +228,6 @@ def bench_paged(torch, api, spec, warmup, steps, key):
             "algorithmic_bytes_per_launch": unique_kv,
             "logical_kv_bytes": kv,
             "launch_us_events": ms * 1e3,
-            "launch_us_min": min(per) * 1e3,
         },
     }
     del dq, dk, dv, dt, dl, ws, o
@@ -240,8 +240,7 @@ def bench_copy(torch, warmup, steps):
     n = 1 << 31
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    per, wall = time_launches(torch, lambda: dst.copy_(src), warmup, steps)
-    ms = sum(per) / len(per)
+    ms, wall = time_launches(torch, lambda: dst.copy_(src), warmup, steps)
     log(f"[bench] copy 2 GiB: {ms * 1e3:.1f} us, {2 * n / (ms * 1e-3) / 1e9:.0f} GB/s (read+write)")
     return {"workload": "copy_2GiB", "bytes_read": n, "bytes_written": n,
             "ms_per_step": wall / steps, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}

@@ -123,10 +123,13 @@ def test_workspace_bytes(api):
     assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 1) == 0
     assert L.attn_paged_workspace_bytes(0, 40, 5, 128, 2048, 16) == 0
     assert L.attn_paged_workspace_bytes(4, 40, 17, 128, 2048, 16) == 0
-    # automatic split count: never more than one split per 16 blocks
-    assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 15, 0) == 0
-    auto = L.attn_paged_workspace_bytes(1, 1, 1, 128, 256, 0)
-    assert auto == 4 * 16 * 129
+    # automatic split count: about 32 blocks per split, raised towards 2048
+    # (split, head, sequence) waves while every split keeps >= 4 blocks
+    assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 15, 0) == 4 * 3 * 129
+    assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 3, 0) == 0
+    assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 256, 0) == 4 * 64 * 129
+    # the 64-sequence x 40-head decode shape with 256-block tables: 8 splits
+    assert L.attn_paged_workspace_bytes(64, 40, 1, 128, 256, 0) == 4 * 64 * 40 * 8 * 129
 
 
 def test_merge_and_gather_reject_bad_arguments(api):
