@@ -82,17 +82,23 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
     return;
   }
 
-  // Q as the B operand: lane holds query l16, d = 32 c + 8 g + (0..7)
+  // Q as the B operand: lane holds query l16, d = 32 c + 8 g + (0..7). A
+  // negative scale is folded into Q (exact sign flip), so the running max is
+  // taken over scores that the exponent multiplies by a positive factor.
+  const bool neg = scale < 0.f;
   bf16x8 qreg[DC];
   {
     const bool ok = l16 < q_len;
     const u32x4* src = reinterpret_cast<const u32x4*>(q + (bhq + (ok ? l16 : 0)) * D + 8 * g);
+    const unsigned flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       u32x4 w = ok ? src[c * 4] : u32x4{0, 0, 0, 0};
+      w ^= flip;
       qreg[c] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  const float sc_abs = neg ? -scale : scale;
 
   const size_t blk_stride = (size_t)H * 16 * D;  // elements per physical block
   const size_t head_off = (size_t)h * 16 * D;
@@ -103,7 +109,9 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   f32x4 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float cs = scale * kLog2e;
+  // exp(scale*(s-m)) == 2^(cs*(s-m)); cs stays positive so that a masked score
+  // (-inf) still gives P = 0 when scale is 0
+  const float cs = fmaxf(sc_abs * kLog2e, 1e-30f);
 
   // K operands (row l16 of each slab) and V pieces (contiguous per instruction)
   // of the block pair n, n+1. A missing second block reads as zeros.
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   l_tot = sum_xor32(l_tot);
   if (l16 < q_len) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float row_lse = l_tot > 0.f ? scale * m_run + __logf(l_tot) : -INFINITY;
+    const float row_lse = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
     if (num_splits == 1) {
       bf16* dst = o + (bhq + l16) * D;
 #pragma unroll

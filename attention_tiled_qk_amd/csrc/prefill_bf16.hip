@@ -9,27 +9,31 @@
 //
 // gfx950 mapping (per workgroup of NW waves, BM = 32 * NW query rows):
 //   * K/V tiles move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
-//     register round trip) into ST rotating stages, so tile j+ST-1 is in flight
-//     while tile j is consumed; one barrier per tile. The buffer descriptor of
-//     each tile ends at the head's last key, so rows past L arrive as zeros.
+//     register round trip). K and V have two LDS stages each: while K_{j+1} and
+//     V_j are read, K_{j+2} and V_{j+1} are in flight; one barrier per tile.
+//     The buffer descriptor of each tile ends at the head's last key, so rows
+//     past L arrive as zeros.
 //   * LDS tiles are unpadded; 16-byte chunks are XOR-swizzled per row (a
 //     different swizzle for K and for V) so that the K operand reads and the
 //     transposing V reads below are free of bank conflicts. The swizzle is
 //     applied on the load side by choosing which global chunk each lane fetches.
 //   * each wave owns 32 query rows; Q stays in VGPRs as the B operand of
 //     S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so every lane's accumulators hold
-//     keys of ONE query: the row max / row sum are in-lane reductions plus one
-//     permlane32 swap, and the O^T accumulator keeps one query per lane too;
+//     keys of ONE query: row sums are in-lane plus one permlane32 swap, and the
+//     O^T accumulator keeps one query per lane too;
 //   * P^T feeds O^T += V^T P^T straight from the S^T accumulators (converted to
 //     bf16 in registers); V^T operands come from the row-major V tile through
 //     ds_read_b64_tr_b16 transposing reads;
-//   * the running max is only moved when a row's maximum grows by more than
-//     2^8 in exp2 units. Any reference value m gives the same O = sum(e^(s-m) v)
-//     / sum(e^(s-m)); keeping a stale m bounds P by 2^8 and skips the rescale of
-//     the accumulators on almost every tile;
+//   * software pipelining: iteration j issues the QK^T products of tile j+1 in
+//     the same basic block as the exponentials of tile j, so one wave's matrix
+//     cores and vector ALUs work at the same time;
+//   * reference max: any reference m gives the same O = sum(e^(s-m) v) /
+//     sum(e^(s-m)). The exponentials use the current m; only when a lane's P
+//     sum over a tile reaches 2^30 (or m is unset) is the row max taken, m
+//     moved, l and O rescaled and P recomputed -- rare after the first tile;
 //   * causal: key tiles above a wave's last row are skipped, the mask is only
-//     evaluated on tiles that cross the diagonal, workgroups are ordered
-//     heavy-first within a head and heads are kept on one XCD (xcd_remap).
+//     evaluated on tiles that cross the diagonal, and the work order (tile_of)
+//     keeps each head on one XCD and starts the longest query tiles first.
 #include <type_traits>
 
 #include "common.h"
@@ -38,10 +42,9 @@ namespace attn {
 
 namespace {
 
-constexpr float kRescaleLog2 = 8.f;           // move m only when P could exceed 2^8
 constexpr float kMaxTileSum = 1073741824.f;   // 2^30: bound on one lane's P sum per tile
 
-template <int D, int NW, int BN, int ST>
+template <int D, int NW, int BN>
 struct PrefillCfg {
   static constexpr int BM = 32 * NW;        // query rows per workgroup
   static constexpr int KC = D / 16;         // 16-wide k chunks of the QK^T contraction
@@ -56,7 +59,6 @@ struct PrefillCfg {
   static constexpr int LOADS = 2 * PPW;     // buffer loads per wave per tile
   static constexpr int THREADS = NW * 64;
   static_assert(PIECES % NW == 0 && PPW >= 1, "tile pieces must split evenly over the waves");
-  static_assert(ST == 2 || ST == 3, "two or three LDS stages");
   static_assert(BN % 32 == 0, "key tile is a multiple of 32");
 };
 
@@ -90,256 +92,11 @@ __device__ __forceinline__ void tile_of(int id, int n_heads, int n_qtiles, int& 
 
 }  // namespace
 
-template <int D, int NW, int BN, int ST, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int L, int n_qtiles, float scale) {
-  using C = PrefillCfg<D, NW, BN, ST>;
-  // one object per stage, so the compiler can tell the stages' LDS-DMA writes apart
-  __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char ks2[ST > 2 ? C::TILEB : 16];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs2[ST > 2 ? C::TILEB : 16];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int g = lane >> 5;  // half-wave: k group of the 32x32 operands
-
-  // ---- which (head, q-tile) this workgroup owns: head-major, heavy tiles first
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = id / n_qtiles;
-  const int qt = CAUSAL ? (n_qtiles - 1 - id % n_qtiles) : (id % n_qtiles);
-  const size_t head_off = (size_t)bh * L * D;
-  const bf16* kh = k + head_off;
-  const bf16* vh = v + head_off;
-
-  const int q0 = qt * C::BM;
-  const int wrow0 = q0 + wave * 32;
-  const int my_row = wrow0 + l32;
-
-  const int n_kt = CAUSAL ? (min(q0 + C::BM, L) - 1) / BN + 1 : (L + BN - 1) / BN;
-
-  // ---- per-lane offsets of the loads into LDS (fixed across tiles)
-  unsigned koff[C::PPW], voff[C::PPW];
-#pragma unroll
-  for (int i = 0; i < C::PPW; ++i) {
-    const int piece = wave + NW * i;
-    const int row = piece * C::RPP + lane / C::NCH;
-    const int phys = lane % C::NCH;
-    koff[i] = row * C::ROWB + (phys ^ kswz<C::NCH>(row)) * 16;
-    voff[i] = row * C::ROWB + (phys ^ vswz<C::NCH>(row)) * 16;
-  }
-  auto kst = [&](auto s) -> ATTN_LDS unsigned char* {
-    if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)ks0;
-    else if constexpr (decltype(s)::value == 1) return (ATTN_LDS unsigned char*)ks1;
-    else return (ATTN_LDS unsigned char*)ks2;
-  };
-  auto vst = [&](auto s) -> ATTN_LDS unsigned char* {
-    if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)vs0;
-    else if constexpr (decltype(s)::value == 1) return (ATTN_LDS unsigned char*)vs1;
-    else return (ATTN_LDS unsigned char*)vs2;
-  };
-  auto issue = [&](auto s, int kt) {
-    const int rows_left = L - kt * BN;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kh + (size_t)kt * BN * D, rows_left * C::ROWB);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vh + (size_t)kt * BN * D, rows_left * C::ROWB);
-#pragma unroll
-    for (int i = 0; i < C::PPW; ++i) dma16(rk, kst(s) + (wave + NW * i) * 1024, koff[i]);
-#pragma unroll
-    for (int i = 0; i < C::PPW; ++i) dma16(rv, vst(s) + (wave + NW * i) * 1024, voff[i]);
-  };
-
-  // ---- per-lane LDS read offsets (fixed across tiles and stages)
-  // K operand, chunk kc: row l32 (+32 per key block), logical chunk 2 kc + g
-  int kaddr[C::KC];
-#pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc)
-    kaddr[kc] = l32 * C::ROWB + (((2 * kc + g) ^ kswz<C::NCH>(l32)) * 16);
-  // V^T operand, column block db: the transposing read of lane (grp, i16)
-  // addresses row 4 g + i16/4 (+16 per 16-key chunk, +8 for the second half)
-  // and columns db*32 + 16 (grp & 1) + 4 (i16 & 3) .. +3
-  int vaddr[C::DB];
-  {
-    const int i16 = lane & 15;
-    const int grp = lane >> 4;
-    const int r = 4 * g + (i16 >> 2);
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int c = db * 4 + 2 * (grp & 1) + ((i16 & 3) >> 1);
-      vaddr[db] = r * C::ROWB + ((c ^ vswz<C::NCH>(r)) * 16) + 8 * (i16 & 1);
-    }
-  }
-
-  // ---- Q (B operand: lane holds d = 16 kc + 8 g + 0..7). A negative scale is
-  // folded into Q (exact sign flip) so the running max is always taken over
-  // scores that the exponent multiplies by a positive factor.
-  const bool neg = scale < 0.f;
-  const float sc_abs = neg ? -scale : scale;
-  bf16x8 qreg[C::KC];
-  {
-    const bool ok = my_row < L;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + head_off + (size_t)(ok ? my_row : 0) * D + 8 * g);
-    const unsigned flip = neg ? 0x80008000u : 0u;
-#pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      u32x4 w = ok ? src[kc * 2] : u32x4{0, 0, 0, 0};
-      w ^= flip;
-      qreg[kc] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-
-  // ---- start streaming K/V (after Q, so the in-order load counter covers Q first)
-  issue(std::integral_constant<int, 0>{}, 0);
-  if constexpr (ST == 3) {
-    if (n_kt > 1) issue(std::integral_constant<int, 1>{}, 1);
-  }
-
-  float m_run = -INFINITY;  // raw-score units
-  float l_run = 0.f;
-  f32x16 acc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-  const float c = sc_abs * kLog2e;  // exp(scale*(s-m)) == 2^(c*(s-m))
-
-  auto compute = [&](auto s, int kt) {
-    const int key0 = kt * BN;
-    if (CAUSAL && key0 > wrow0 + 31) return;  // every row of this wave precedes the tile
-    const ATTN_LDS unsigned char* kb_ = kst(s);
-    const ATTN_LDS unsigned char* vb_ = vst(s);
-
-    f32x16 sc[C::NKB];
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      sc[kb] = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kb_ + kaddr[kc] + kb * 32 * C::ROWB);
-        sc[kb] = mfma32(a, qreg[kc], sc[kb]);
-      }
-    }
-
-    // mask where the tile reaches past the wave's first row (causal) or past L
-    const bool need_mask = CAUSAL ? (key0 + BN - 1 > wrow0) : (key0 + BN > L);
-    if (need_mask) {
-      // key of sc[kb][j] is key0 + kb*32 + 8 (j/4) + 4 g + j%4
-      const int lim = (CAUSAL ? my_row : L - 1) - key0 - 4 * g;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          sc[kb][j] = (kb * 32 + 8 * (j >> 2) + (j & 3) <= lim) ? sc[kb][j] : -INFINITY;
-    }
-
-    float mt = sc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int j = (kb == 0 ? 1 : 0); j < 16; ++j) mt = fmaxf(mt, sc[kb][j]);
-    mt = max_xor32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    // NaN (both -inf: nothing visible yet) compares false and leaves m alone
-    if (__builtin_amdgcn_ballot_w64((m_new - m_run) * c > kRescaleLog2) != 0) {
-      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = (m_run == -INFINITY ? 0.f : m_run) * c;
-
-    // P = 2^(c s - c m) as the bf16 B operands of O^T += V^T P^T
-    bf16x8 p[2 * C::NKB];
-    float part[2 * C::NKB];
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = exp2_fast(__builtin_fmaf(sc[kb][8 * h + i], c, -mc));
-        part[2 * kb + h] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        u32x4 w;
-        w[0] = pack_bf16x2(e[0], e[1]);
-        w[1] = pack_bf16x2(e[2], e[3]);
-        w[2] = pack_bf16x2(e[4], e[5]);
-        w[3] = pack_bf16x2(e[6], e[7]);
-        p[2 * kb + h] = __builtin_bit_cast(bf16x8, w);
-      }
-    float lsum = part[0];
-#pragma unroll
-    for (int i = 1; i < 2 * C::NKB; ++i) lsum += part[i];
-    l_run += lsum;
-
-    // chunk cidx covers keys 16 cidx .. +15; this lane's P elements 0..3 are keys
-    // 16 cidx + 4 g + 0..3 and elements 4..7 are keys 16 cidx + 8 + 4 g + 0..3
-#pragma unroll
-    for (int cidx = 0; cidx < 2 * C::NKB; ++cidx) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const ATTN_LDS unsigned char* base = vb_ + vaddr[db] + cidx * 16 * C::ROWB;
-        const bf16x4 lo = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base));
-        const bf16x4 hi = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base + 8 * C::ROWB));
-        acc[db] = mfma32(join(lo, hi), p[cidx], acc[db]);
-      }
-    }
-  };
-
-  // stage S holds tile kt; on entry tiles kt .. kt+ST-2 may still be in flight
-  auto step = [&](auto s, int kt) {
-    constexpr int S = decltype(s)::value;
-    if constexpr (ST == 3) {
-      if (kt + 1 < n_kt) wait_vmcnt<C::LOADS>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1's stage
-    if (kt + ST - 1 < n_kt) issue(std::integral_constant<int, (S + ST - 1) % ST>{}, kt + ST - 1);
-    compute(s, kt);
-  };
-
-  for (int kt = 0; kt < n_kt; kt += ST) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
-    if constexpr (ST == 3) {
-      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
-    }
-  }
-
-  // ---- epilogue: O = O / l, lse = scale * m + ln l
-  const float l_tot = sum_xor32(l_run);
-  if (my_row < L) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = o + head_off + (size_t)my_row * D;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = db * 32 + 8 * jj + 4 * g;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    if (lse != nullptr && g == 0)
-      lse[(size_t)bh * L + my_row] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
-  }
-}
-
-// Software-pipelined form of the same computation. Iteration j issues the
-// QK^T products of tile j+1 in the same instruction stream as the softmax of
-// tile j, so the matrix cores and the vector ALUs of one wave work at the same
-// time; then it accumulates P_j V_j. K and V have two LDS stages each: K_{j+2}
-// and V_{j+1} are loaded while K_{j+1} and V_j are read.
 template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int L, int n_heads, int n_qtiles, float scale) {
-  using C = PrefillCfg<D, NW, BN, 2>;
+  using C = PrefillCfg<D, NW, BN>;
   __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILEB];
@@ -433,7 +190,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-  const float c = sc_abs * kLog2e;
+  // exp(scale*(s-m)) == 2^(c*(s-m)); c is kept positive so that a masked score
+  // (-inf) still gives P = 0 when scale is 0 (c*s then underflows to 0)
+  const float c = fmaxf(sc_abs * kLog2e, 1e-30f);
 
   auto qk = [&](f32x16* sc, const ATTN_LDS unsigned char* kb_) {
 #pragma unroll
@@ -492,7 +251,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int j = (kb == 0 ? 1 : 0); j < 16; ++j) mt = fmaxf(mt, sc[kb][j]);
     mt = max_xor32(mt);
     const float m_new = fmaxf(m_run, mt);
-    // m = -inf before gives 0; an unchanged m (also -inf == -inf) gives 1
+    // an unchanged m (also -inf == -inf) gives 1; m = -inf before gives 0
     const float alpha = m_new == m_run ? 1.f : exp2_fast((m_run - m_new) * c);
     m_run = m_new;
     mc_run = (m_run == -INFINITY ? 0.f : m_run) * c;
@@ -602,26 +361,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 template <int D, int NW, int BN, bool CAUSAL>
 hipError_t launch_prefill_pipe(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int L, float scale, hipStream_t stream) {
-  using C = PrefillCfg<D, NW, BN, 2>;
+  using C = PrefillCfg<D, NW, BN>;
   const int n_qtiles = (L + C::BM - 1) / C::BM;
   const long long grid = (long long)B * H * n_qtiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_bf16_pipe_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)grid),
                      dim3(C::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                      (bf16*)o, lse, L, B * H, n_qtiles, scale);
-  return hipGetLastError();
-}
-
-template <int D, int NW, int BN, int ST, bool CAUSAL>
-hipError_t launch_prefill_variant(const void* q, const void* k, const void* v, void* o, float* lse,
-                                  int B, int H, int L, float scale, hipStream_t stream) {
-  using C = PrefillCfg<D, NW, BN, ST>;
-  const int n_qtiles = (L + C::BM - 1) / C::BM;
-  const long long grid = (long long)B * H * n_qtiles;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BN, ST, CAUSAL>), dim3((unsigned)grid),
-                     dim3(C::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                     (bf16*)o, lse, L, n_qtiles, scale);
   return hipGetLastError();
 }
 

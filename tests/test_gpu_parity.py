@@ -125,6 +125,57 @@ def test_prefill_full_size_sampled(api, spec, pairs):
     assert torch.isfinite(o.float()).all()
 
 
+def _prefill_vs_oracle(api, q, k, v, scale, causal, tol):
+    ref_o, ref_lse = oracle.prefill(q, k, v, scale, causal)
+    o, lse = api.attn_prefill(*to_dev(q, k, v), causal=causal, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    e = max_err(o, ref_o)
+    el = lse_err(lse, ref_lse)
+    say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= tol and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_growing_scores(api, causal):
+    """Scores that keep growing along the keys: every query has a component of
+    about 3 along d = 0 and key j one of 11 j, so a row's scores rise by about
+    2.9 per key and its maximum outgrows the reference max (by 2^30 in the
+    exponent) many times over the sequence."""
+    g = torch.Generator().manual_seed(31)
+    B, H, L, D = 1, 2, 700, 128
+    q = torch.randn(B, H, L, D, generator=g)
+    k = torch.randn(B, H, L, D, generator=g)
+    v = torch.randn(B, H, L, D, generator=g)
+    q[..., 0] += 3.0
+    k[..., 0] += 11.0 * torch.arange(L, dtype=torch.float32)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    _prefill_vs_oracle(api, q, k, v, 1.0 / math.sqrt(D), causal, TOL_BF16)
+
+
+def test_prefill_late_outlier_key(api):
+    """One key far above all others late in the sequence: every row that sees it
+    must move its reference max there and rescale what it accumulated."""
+    g = torch.Generator().manual_seed(32)
+    B, H, L, D = 1, 2, 640, 128
+    q = torch.randn(B, H, L, D, generator=g)
+    k = torch.randn(B, H, L, D, generator=g)
+    v = torch.randn(B, H, L, D, generator=g)
+    q[..., 0] += 3.0
+    k[:, :, 500, 0] = 2000.0
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    _prefill_vs_oracle(api, q, k, v, 1.0 / math.sqrt(D), True, TOL_BF16)
+
+
+@pytest.mark.parametrize("scale", [-1.0 / math.sqrt(128), 0.0, 0.5])
+def test_prefill_other_scales(api, scale):
+    """Negative, zero and large scales (the reference max is taken over
+    scale-signed scores; scale 0 gives the mean of the visible values)."""
+    spec = PrefillSpec("scales", 1, 2, 300, 128, "bf16", True, 33)
+    q, k, v = prefill_inputs(spec)
+    _prefill_vs_oracle(api, q, k, v, scale, True, TOL_BF16)
+
+
 def test_prefill_deterministic(api):
     q, k, v = to_dev(*prefill_inputs(PrefillSpec("d", 2, 2, 300, 128, "bf16", True, 5)))
     o1 = api.attn_prefill(q, k, v)
@@ -196,6 +247,30 @@ def test_paged_small(api, lens, q_len, splits, causal):
     say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
     assert torch.isfinite(o.float()).all()
     assert e <= TOL_BF16 and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("splits", [1, 2, 0])
+def test_paged_long_split_crosses_id_chunks(api, splits):
+    """Splits longer than the 256 block ids the kernel stages at a time."""
+    inp = _paged((4200, 9000, 300), 5, H=2, seed=41, extra=3)
+    scale = 1.0 / math.sqrt(128)
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, scale, True)
+    o, lse = _run_paged(api, inp, splits)
+    e = max_err(o, ref_o)
+    say(f"  splits={splits} max|dO|={e:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= TOL_BF16 and lse_err(lse, ref_lse) <= TOL_LSE
+
+
+@pytest.mark.parametrize("scale", [-1.0 / math.sqrt(128), 0.0])
+def test_paged_other_scales(api, scale):
+    inp = _paged((5, 100, 257, 1000), 5, seed=42)
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, scale, True)
+    o, lse = _run_paged(api, inp, 3, True, scale)
+    assert torch.isfinite(o.float()).all()
+    assert max_err(o, ref_o) <= TOL_BF16 and lse_err(lse, ref_lse) <= TOL_LSE
 
 
 def test_paged_d64(api):
