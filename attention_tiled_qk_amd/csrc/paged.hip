@@ -28,8 +28,11 @@ namespace attn {
 
 constexpr int kIdChunk = 256;  // block ids staged in LDS at a time (even)
 
-template <int D>
-__global__ __launch_bounds__(64) void paged_attn_kernel(
+// WPS waves per workgroup share one (split, head, sequence): wave w takes the
+// w-th part of the split's blocks and the parts are merged in LDS at the end,
+// which gives short-split launches more waves without more partials.
+template <int D, int WPS>
+__global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_pool, const bf16* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o_part,
@@ -40,12 +43,13 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   constexpr int PV = D * 2 + 64;        // LDS row pitch of a V slab (bytes)
   constexpr int VCH = 16 * D / 8 / 64;  // 16-byte pieces of one slab per lane
   constexpr int CPR = D / 8;            // 16-byte pieces per slab row
-  __shared__ __attribute__((aligned(16))) unsigned char vlds_raw[2 * 16 * PV];
-  __shared__ int ids_raw[kIdChunk];
-  ATTN_LDS unsigned char* vlds = (ATTN_LDS unsigned char*)vlds_raw;
-  ATTN_LDS int* ids = (ATTN_LDS int*)ids_raw;
+  __shared__ __attribute__((aligned(16))) unsigned char vlds_raw[WPS][2 * 16 * PV];
+  __shared__ int ids_raw[WPS][kIdChunk];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  ATTN_LDS unsigned char* vlds = (ATTN_LDS unsigned char*)vlds_raw[wave];
+  ATTN_LDS int* ids = (ATTN_LDS int*)ids_raw[wave];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int split = blockIdx.x;
@@ -64,7 +68,7 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   const size_t bhq = ((size_t)b * H + h) * q_len;  // row of (b, h, query 0)
 
   if (blk0 >= blk1) {  // empty split: contributes nothing to the merge
-    if (l16 < q_len) {
+    if (wave == 0 && l16 < q_len) {
       if (num_splits == 1) {  // only for seq_len == 0, outside the contract
         bf16* dst = o + (bhq + l16) * D;
 #pragma unroll
@@ -228,11 +232,19 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
     }
   };
 
+  // this wave's part of the split: an even number of blocks for every wave
+  // but the last, so block pairs never straddle two waves
+  const int part = ((blk1 - blk0 + WPS - 1) / WPS + 1) & ~1;
+  const int w0 = min(blk0 + wave * part, blk1);
+  const int w1 = min(w0 + part, blk1);
+  c0 = w0;
+  c1 = w0;
+
   // Chunks of up to kIdChunk blocks (an even number, so block pairs never
   // straddle chunks). Within a chunk the loads are software-pipelined: the
   // K/V of pair n+2 are in flight while pair n is computed.
-  for (; c0 < blk1; c0 = c1) {
-    c1 = min(c0 + kIdChunk, blk1);
+  for (; c0 < w1; c0 = c1) {
+    c1 = min(c0 + kIdChunk, w1);
     for (int i = lane; i < c1 - c0; i += 64) ids[i] = table[c0 + i];
     Pair r0, r1;
     load(c0, r0);
@@ -246,6 +258,34 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
       n += 2;
       if (n >= c1) break;
     }
+  }
+
+  if constexpr (WPS > 1) {
+    // merge the waves' states lane by lane (equal lanes hold the same query,
+    // output columns and key positions) into wave 0, through LDS
+    static_assert(WPS == 2, "two waves per split");
+    __syncthreads();  // both waves are done with their LDS staging areas
+    float* xch = (float*)vlds_raw[1];  // (2 + 4 DB) floats per lane
+    if (wave == 1) {
+      xch[lane] = m_run;
+      xch[64 + lane] = l_run;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xch[128 + (db * 4 + j) * 64 + lane] = acc[db][j];
+    }
+    __syncthreads();
+    if (wave == 1) return;
+    const float m1 = xch[lane];
+    const float m_new = fmaxf(m_run, m1);
+    const float a0 = m_run == m_new ? 1.f : exp2_fast((m_run - m_new) * cs);  // 0 when m_run = -inf
+    const float a1 = m1 == m_new ? 1.f : exp2_fast((m1 - m_new) * cs);
+    l_run = a0 * l_run + a1 * xch[64 + lane];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[db][j] = a0 * acc[db][j] + a1 * xch[128 + (db * 4 + j) * 64 + lane];
+    m_run = m_new;
   }
 
   // ---- epilogue
@@ -274,7 +314,9 @@ __global__ __launch_bounds__(64) void paged_attn_kernel(
   }
 }
 
-// Cross-split reduction: one workgroup of D threads per output row.
+// Cross-split reduction: one workgroup of D threads per output row. The loops
+// over the partials are unrolled by 8 so that their loads are in flight
+// together (the kernel is latency-bound: a row is only S (D + 1) floats).
 template <int D, typename OutT>
 __global__ __launch_bounds__(D) void lse_merge_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
@@ -283,12 +325,34 @@ __global__ __launch_bounds__(D) void lse_merge_kernel(const float* __restrict__ 
   const size_t row = blockIdx.x;
   const int d = threadIdx.x;
   const float* lp = lse_part + row * S;
+  const float* op = o_part + row * S * D + d;
   float m = -INFINITY;
-  for (int p = 0; p < S; ++p) m = fmaxf(m, lp[p]);
+  int p = 0;
+  for (; p + 8 <= S; p += 8) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = lp[p + i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, t[i]);
+  }
+  for (; p < S; ++p) m = fmaxf(m, lp[p]);
   float acc = 0.f, wsum = 0.f;
   if (m != -INFINITY) {
-    const float* op = o_part + row * S * D + d;
-    for (int p = 0; p < S; ++p) {
+    for (p = 0; p + 8 <= S; p += 8) {
+      float lv[8], ov[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lv[i] = lp[p + i];
+        ov[i] = op[(size_t)(p + i) * D];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float w = lv[i] == -INFINITY ? 0.f : expf(lv[i] - m);
+        wsum += w;
+        acc = __builtin_fmaf(w, ov[i], acc);
+      }
+    }
+    for (; p < S; ++p) {
       const float lv = lp[p];
       const float w = lv == -INFINITY ? 0.f : expf(lv - m);
       wsum += w;
@@ -321,20 +385,41 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(const bf16* __restric
   *reinterpret_cast<u32x4*>(out + dst) = *reinterpret_cast<const u32x4*>(pool + src);
 }
 
+template <int D, int WPS>
+static void launch_paged_variant(dim3 grid, hipStream_t stream, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables,
+                                 const int32_t* seq_lens, void* o, float* lse, float* o_part,
+                                 float* lse_part, int H, int q_len, int max_blocks, int num_splits,
+                                 int causal, float scale) {
+  hipLaunchKernelGGL((paged_attn_kernel<D, WPS>), grid, dim3(64 * WPS), 0, stream, (const bf16*)q,
+                     (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
+                     lse, o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+}
+
 hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_pool,
                              const int32_t* block_tables, const int32_t* seq_lens, void* o,
                              float* lse, float* o_part, float* lse_part, int B, int H, int q_len,
                              int D, int max_blocks, int num_splits, int causal, float scale,
                              hipStream_t stream) {
   dim3 grid(num_splits, H, B);
-  if (D == 128)
-    hipLaunchKernelGGL(paged_attn_kernel<128>, grid, dim3(64), 0, stream, (const bf16*)q,
-                       (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
-                       lse, o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
-  else
-    hipLaunchKernelGGL(paged_attn_kernel<64>, grid, dim3(64), 0, stream, (const bf16*)q,
-                       (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
-                       lse, o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+  // With few (split, head, sequence) items the resident waves would leave part
+  // of the chip idle in the last round; give each item two waves instead.
+  const bool two = (long long)num_splits * H * B < 4096;
+  if (D == 128) {
+    if (two)
+      launch_paged_variant<128, 2>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
+                                   o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+    else
+      launch_paged_variant<128, 1>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
+                                   o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+  } else {
+    if (two)
+      launch_paged_variant<64, 2>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
+                                  o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+    else
+      launch_paged_variant<64, 1>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
+                                  o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+  }
   return hipGetLastError();
 }
 
