@@ -18,6 +18,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
+    "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes",
     "attn_lse_merge", "attn_paged_gather", "attn_version", "lib", "LIB_PATH",
     "ATTN_F32", "ATTN_BF16",
 ]
@@ -44,6 +45,11 @@ lib.attn_paged_workspace_bytes.restype = _sz
 lib.attn_paged_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                                   _f, _i, _p, _sz, _i, _p]
 lib.attn_paged_decode.restype = _i
+lib.attn_paged_gqa_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+lib.attn_paged_gqa_workspace_bytes.restype = _sz
+lib.attn_paged_decode_gqa.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                      _i, _f, _i, _p, _sz, _i, _p]
+lib.attn_paged_decode_gqa.restype = _i
 lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
@@ -130,6 +136,11 @@ def attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits=0)
     return int(lib.attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits))
 
 
+def attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, max_blocks_per_seq, num_splits=0):
+    return int(lib.attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, max_blocks_per_seq,
+                                                  num_splits))
+
+
 def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True, scale=None,
                       num_splits=0, o=None, lse=None, return_lse=False, workspace=None,
                       stream=None):
@@ -138,6 +149,8 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
     k_pool, v_pool [num_blocks, H, 16, D] bf16; block_tables [B, W] int32;
     seq_lens [B] int32 (key counts including the q_len new tokens). A float32
     workspace is allocated here when the split count needs one and none is given.
+    When the pools hold fewer heads than q (a divisor of them), the call goes to
+    attn_paged_decode_gqa (grouped-query attention).
     """
     _dev(q, "q", torch.bfloat16)
     _dev(k_pool, "k_pool", torch.bfloat16)
@@ -145,11 +158,11 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
     _dev(block_tables, "block_tables", torch.int32)
     _dev(seq_lens, "seq_lens", torch.int32)
     if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
-        raise ValueError("q must be [B, H, q_len, D] and the pools [num_blocks, H, 16, D]")
-    B, H, q_len, D = q.shape
-    nblk, Hp, bs, Dp = k_pool.shape
-    if Hp != H or Dp != D:
-        raise ValueError("pool heads / head_dim must match q")
+        raise ValueError("q must be [B, Hq, q_len, D] and the pools [num_blocks, Hkv, 16, D]")
+    B, Hq, q_len, D = q.shape
+    nblk, Hkv, bs, Dp = k_pool.shape
+    if Dp != D or Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("pool head_dim must match q and pool heads must divide query heads")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, W] and seq_lens [B]")
     width = block_tables.shape[1]
@@ -159,18 +172,23 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
         o = torch.empty_like(q)
     _dev(o, "o", torch.bfloat16)
     if return_lse and lse is None:
-        lse = torch.empty((B, H, q_len), device=q.device, dtype=torch.float32)
+        lse = torch.empty((B, Hq, q_len), device=q.device, dtype=torch.float32)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
-    need = attn_paged_workspace_bytes(B, H, q_len, D, width, num_splits)
+    need = attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, width, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.attn_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-                               _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, q_len, D, nblk, width,
-                               bs, int(bool(causal)), float(scale), int(num_splits),
-                               _ptr(workspace), ws_bytes, ATTN_BF16, _stream(q.device, stream))
-    _check(st, "attn_paged_decode")
+    common = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), _ptr(o),
+              _ptr(lse), B)
+    tail = (q_len, D, nblk, width, bs, int(bool(causal)), float(scale), int(num_splits),
+            _ptr(workspace), ws_bytes, ATTN_BF16, _stream(q.device, stream))
+    if Hq == Hkv:
+        st = lib.attn_paged_decode(*common, Hq, *tail)
+        _check(st, "attn_paged_decode")
+    else:
+        st = lib.attn_paged_decode_gqa(*common, Hq, Hkv, *tail)
+        _check(st, "attn_paged_decode_gqa")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

@@ -16,7 +16,7 @@ hipError_t launch_prefill_bf16(const void*, const void*, const void*, void*, flo
 hipError_t launch_prefill_f32(const void*, const void*, const void*, void*, float*, int, int, int,
                               int, int, float, hipStream_t);
 hipError_t launch_paged_attn(const void*, const void*, const void*, const int32_t*,
-                             const int32_t*, void*, float*, float*, float*, int, int, int, int,
+                             const int32_t*, void*, float*, float*, float*, int, int, int, int, int,
                              int, int, int, float, hipStream_t);
 hipError_t launch_lse_merge(const float*, const float*, void*, float*, long long, int, int, int,
                             hipStream_t);
@@ -112,13 +112,81 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   return hip_status(attn::launch_prefill_f32(q, k, v, o, lse, B, H, L, D, causal, scale, s));
 }
 
-size_t attn_paged_workspace_bytes(int B, int H, int q_len, int D, int max_blocks_per_seq,
-                                  int num_splits) {
-  if (B <= 0 || H <= 0 || q_len <= 0 || q_len > ATTN_PAGED_MAX_QLEN) return 0;
+}  // extern "C"
+
+namespace {
+
+// Split count the library uses for `Hkv` KV heads (one wave group per split, KV
+// head and sequence) when the caller passes num_splits = 0.
+int splits_for(int B, int Hkv, int max_blocks_per_seq, int num_splits) {
+  return num_splits == 0 ? auto_splits(B, Hkv, max_blocks_per_seq) : num_splits;
+}
+
+size_t paged_workspace(int B, int Hq, int Hkv, int q_len, int D, int max_blocks_per_seq,
+                       int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || q_len <= 0 || Hq % Hkv != 0) return 0;
+  if ((long long)(Hq / Hkv) * q_len > ATTN_PAGED_MAX_QLEN) return 0;
   if (D != 64 && D != 128) return 0;
   if (max_blocks_per_seq <= 0 || num_splits < 0 || num_splits > ATTN_PAGED_MAX_SPLITS) return 0;
-  const int S = num_splits == 0 ? auto_splits(B, H, max_blocks_per_seq) : num_splits;
-  return workspace_for(B, H, q_len, D, S);
+  return workspace_for(B, Hq, q_len, D, splits_for(B, Hkv, max_blocks_per_seq, num_splits));
+}
+
+int paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse, int B,
+                 int Hq, int Hkv, int q_len, int D, int num_blocks, int max_blocks_per_seq,
+                 int block_size, int causal, float scale, int num_splits, void* workspace,
+                 size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !o) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || q_len <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != ATTN_BLOCK_SIZE) return ATTN_ERR_UNSUPPORTED;
+  const int group = Hq / Hkv;
+  if ((long long)group * q_len > ATTN_PAGED_MAX_QLEN) return ATTN_ERR_UNSUPPORTED;
+  if (num_splits < 0 || num_splits > ATTN_PAGED_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+  if (Hkv > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({num_blocks, Hkv, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
+      checked_mul({B, Hq, q_len, D, 2}) < 0 || (long long)max_blocks_per_seq * 16 > 0x7fffffffLL)
+    return ATTN_ERR_OVERFLOW;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
+    return ATTN_ERR_MISALIGNED;
+  if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
+    return ATTN_ERR_MISALIGNED;
+  const int S = splits_for(B, Hkv, max_blocks_per_seq, num_splits);
+  const size_t need = workspace_for(B, Hq, q_len, D, S);
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+    o_part = static_cast<float*>(workspace);
+    lse_part = o_part + (size_t)B * Hq * q_len * S * D;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = attn::launch_paged_attn(q, k_pool, v_pool, block_tables, seq_lens, o, lse, o_part,
+                                         lse_part, B, Hkv, group, q_len, D, max_blocks_per_seq, S,
+                                         causal, scale, s);
+  if (e != hipSuccess || S == 1) return hip_status(e);
+  return hip_status(attn::launch_lse_merge(o_part, lse_part, o, lse, (long long)B * Hq * q_len, S,
+                                           D, 1, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_paged_workspace_bytes(int B, int H, int q_len, int D, int max_blocks_per_seq,
+                                  int num_splits) {
+  return paged_workspace(B, H, H, q_len, D, max_blocks_per_seq, num_splits);
+}
+
+size_t attn_paged_gqa_workspace_bytes(int B, int Hq, int Hkv, int q_len, int D,
+                                      int max_blocks_per_seq, int num_splits) {
+  return paged_workspace(B, Hq, Hkv, q_len, D, max_blocks_per_seq, num_splits);
 }
 
 int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -126,41 +194,20 @@ int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                       int B, int H, int q_len, int D, int num_blocks, int max_blocks_per_seq,
                       int block_size, int causal, float scale, int num_splits, void* workspace,
                       size_t workspace_bytes, int dtype, void* stream) {
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !o) return ATTN_ERR_NULL_PTR;
-  if (B <= 0 || H <= 0 || q_len <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
-    return ATTN_ERR_BAD_SHAPE;
-  if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
-  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-  if (block_size != ATTN_BLOCK_SIZE) return ATTN_ERR_UNSUPPORTED;
-  if (q_len > ATTN_PAGED_MAX_QLEN) return ATTN_ERR_UNSUPPORTED;
-  if (num_splits < 0 || num_splits > ATTN_PAGED_MAX_SPLITS) return ATTN_ERR_UNSUPPORTED;
-  if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
-  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
-  if (H > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
-  if (checked_mul({num_blocks, H, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
-      (long long)max_blocks_per_seq * 16 > 0x7fffffffLL)
-    return ATTN_ERR_OVERFLOW;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
-    return ATTN_ERR_MISALIGNED;
-  if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
-    return ATTN_ERR_MISALIGNED;
-  const int S = num_splits == 0 ? auto_splits(B, H, max_blocks_per_seq) : num_splits;
-  const size_t need = workspace_for(B, H, q_len, D, S);
-  float* o_part = nullptr;
-  float* lse_part = nullptr;
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return ATTN_ERR_MISALIGNED;
-    o_part = static_cast<float*>(workspace);
-    lse_part = o_part + (size_t)B * H * q_len * S * D;
-  }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = attn::launch_paged_attn(q, k_pool, v_pool, block_tables, seq_lens, o, lse, o_part,
-                                         lse_part, B, H, q_len, D, max_blocks_per_seq, S, causal,
-                                         scale, s);
-  if (e != hipSuccess || S == 1) return hip_status(e);
-  return hip_status(attn::launch_lse_merge(o_part, lse_part, o, lse, (long long)B * H * q_len, S, D,
-                                           1, s));
+  return paged_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, B, H, H, q_len, D,
+                      num_blocks, max_blocks_per_seq, block_size, causal, scale, num_splits,
+                      workspace, workspace_bytes, dtype, stream);
+}
+
+int attn_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse,
+                          int B, int Hq, int Hkv, int q_len, int D, int num_blocks,
+                          int max_blocks_per_seq, int block_size, int causal, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, int dtype,
+                          void* stream) {
+  return paged_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, B, Hq, Hkv, q_len, D,
+                      num_blocks, max_blocks_per_seq, block_size, causal, scale, num_splits,
+                      workspace, workspace_bytes, dtype, stream);
 }
 
 int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int H,

@@ -1,7 +1,9 @@
 // Paged decode / speculative-verify attention, split-KV merge and paged gather.
 //
 // What is computed: for each sequence b and head h, the q_len newest queries
-// attend all seq_len keys of the sequence (bottom-right causal when asked),
+// attend all seq_len keys of the sequence (bottom-right causal when asked);
+// with grouped-query attention `group` query heads share each KV head h and are
+// computed by the same wave from one read of its K/V,
 // where token t of the sequence lives in physical block block_tables[b][t/16],
 // slot t%16 of the K and V pools -- PagedAttention's block table as [P1] §3.2
 // draws it and as the Continuous Batching + PagedAttention item of [P3] passes
@@ -36,8 +38,8 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_pool, const bf16* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int H, int q_len, int max_blocks, int num_splits, int causal,
-    float scale) {
+    float* __restrict__ lse_part, int H, int group, int q_len, int max_blocks, int num_splits,
+    int causal, float scale) {
   constexpr int DC = D / 32;            // 32-wide chunks of the QK^T contraction
   constexpr int DB = D / 16;            // 16-wide output blocks
   constexpr int PV = D * 2 + 64;        // LDS row pitch of a V slab (bytes)
@@ -63,24 +65,29 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   const int blk1 = min(blk0 + per, nb);
   const int key_end = min(seq_len, blk1 * 16);
   const int qpos0 = seq_len - q_len;  // absolute position of query 0
-  const int limit = causal ? qpos0 + l16 : 0x7fffffff;  // last key my query may see
-
-  const size_t bhq = ((size_t)b * H + h) * q_len;  // row of (b, h, query 0)
+  // Column l16 of the MFMA tiles is query t of query head h * group + gi: the
+  // `group` query heads that read KV head h share its K/V loads.
+  const int ncols = group * q_len;
+  const int t = l16 % q_len;
+  const int gi = l16 / q_len;
+  const int limit = causal ? qpos0 + t : 0x7fffffff;  // last key my query may see
+  // row of (b, query head, query t) in q, o, lse and the partials
+  const size_t qrow = (((size_t)b * H + h) * group + (l16 < ncols ? gi : 0)) * q_len + t;
 
   if (blk0 >= blk1) {  // empty split: contributes nothing to the merge
-    if (wave == 0 && l16 < q_len) {
+    if (wave == 0 && l16 < ncols) {
       if (num_splits == 1) {  // only for seq_len == 0, outside the contract
-        bf16* dst = o + (bhq + l16) * D;
+        bf16* dst = o + qrow * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           *reinterpret_cast<u32x2*>(dst + db * 16 + 4 * g) = u32x2{0u, 0u};
-        if (lse != nullptr && g == 0) lse[bhq + l16] = -INFINITY;
+        if (lse != nullptr && g == 0) lse[qrow] = -INFINITY;
       } else {
-        float* dst = o_part + ((bhq + l16) * num_splits + split) * D;
+        float* dst = o_part + (qrow * num_splits + split) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (g == 0) lse_part[(bhq + l16) * num_splits + split] = -INFINITY;
+        if (g == 0) lse_part[qrow * num_splits + split] = -INFINITY;
       }
     }
     return;
@@ -92,8 +99,8 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   const bool neg = scale < 0.f;
   bf16x8 qreg[DC];
   {
-    const bool ok = l16 < q_len;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + (bhq + (ok ? l16 : 0)) * D + 8 * g);
+    const bool ok = l16 < ncols;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + qrow * D + 8 * g);
     const unsigned flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
@@ -291,11 +298,11 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   // ---- epilogue
   float l_tot = sum_xor16(l_run);
   l_tot = sum_xor32(l_tot);
-  if (l16 < q_len) {
+  if (l16 < ncols) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float row_lse = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
     if (num_splits == 1) {
-      bf16* dst = o + (bhq + l16) * D;
+      bf16* dst = o + qrow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         u32x2 w;
@@ -303,13 +310,13 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
         w[1] = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
         *reinterpret_cast<u32x2*>(dst + db * 16 + 4 * g) = w;
       }
-      if (lse != nullptr && g == 0) lse[bhq + l16] = row_lse;
+      if (lse != nullptr && g == 0) lse[qrow] = row_lse;
     } else {
-      float* dst = o_part + ((bhq + l16) * num_splits + split) * D;
+      float* dst = o_part + (qrow * num_splits + split) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = acc[db] * inv;
-      if (g == 0) lse_part[(bhq + l16) * num_splits + split] = row_lse;
+      if (g == 0) lse_part[qrow * num_splits + split] = row_lse;
     }
   }
 }
@@ -389,18 +396,18 @@ template <int D, int WPS>
 static void launch_paged_variant(dim3 grid, hipStream_t stream, const void* q, const void* k_pool,
                                  const void* v_pool, const int32_t* block_tables,
                                  const int32_t* seq_lens, void* o, float* lse, float* o_part,
-                                 float* lse_part, int H, int q_len, int max_blocks, int num_splits,
-                                 int causal, float scale) {
+                                 float* lse_part, int H, int group, int q_len, int max_blocks,
+                                 int num_splits, int causal, float scale) {
   hipLaunchKernelGGL((paged_attn_kernel<D, WPS>), grid, dim3(64 * WPS), 0, stream, (const bf16*)q,
                      (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
-                     lse, o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+                     lse, o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
 }
 
 hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_pool,
                              const int32_t* block_tables, const int32_t* seq_lens, void* o,
-                             float* lse, float* o_part, float* lse_part, int B, int H, int q_len,
-                             int D, int max_blocks, int num_splits, int causal, float scale,
-                             hipStream_t stream) {
+                             float* lse, float* o_part, float* lse_part, int B, int H, int group,
+                             int q_len, int D, int max_blocks, int num_splits, int causal,
+                             float scale, hipStream_t stream) {
   dim3 grid(num_splits, H, B);
   // With few (split, head, sequence) items the resident waves would leave part
   // of the chip idle in the last round; give each item two waves instead.
@@ -408,17 +415,17 @@ hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_po
   if (D == 128) {
     if (two)
       launch_paged_variant<128, 2>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                   o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+                                   o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
     else
       launch_paged_variant<128, 1>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                   o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+                                   o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
   } else {
     if (two)
       launch_paged_variant<64, 2>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                  o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+                                  o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
     else
       launch_paged_variant<64, 1>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                  o_part, lse_part, H, q_len, max_blocks, num_splits, causal, scale);
+                                  o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
   }
   return hipGetLastError();
 }

@@ -15,11 +15,13 @@ The same run also measures, under ``secondary``:
   * c4: paged decode, 64 sequences x 40 heads, q_len 1, lengths U[128, 4096];
   * c5: paged verify, 4 sequences x 40 heads, q_len 5, 32768 keys, shared
     2048-token prefix, 16 splits merged by log-sum-exp;
+  * c4g: grouped-query paged decode, 64 sequences, 64 query heads over 8 KV
+    heads, q_len 1, lengths U[128, 4096];
 each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
-``--only NAME`` runs a single workload (c2, c3, c4, c5, or ``copy``: a plain
+``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, or ``copy``: a plain
 device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
 its entry; that is the form the profiler runs use.
 
@@ -184,25 +186,27 @@ def bench_paged(torch, api, spec, warmup, steps, key):
     dq, dk, dv, dt, dl = (t.cuda() for t in (inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
                                               inp.seq_lens))
     lens = inp.seq_lens.tolist()
-    B, H, q_len, D = inp.q.shape
+    B, Hq, q_len, D = inp.q.shape
+    H = inp.k_pool.shape[1]  # KV heads (fewer than Hq for grouped-query attention)
     width = inp.block_tables.shape[1]
-    ws_bytes = api.attn_paged_workspace_bytes(B, H, q_len, D, width, spec.num_splits)
+    ws_bytes = api.attn_paged_gqa_workspace_bytes(B, Hq, H, q_len, D, width, spec.num_splits)
     ws = torch.empty(max(ws_bytes // 4, 1), device="cuda", dtype=torch.float32)
     o = torch.empty_like(dq)
     api.attn_paged_decode(dq, dk, dv, dt, dl, causal=spec.causal, scale=spec.scale,
                           num_splits=spec.num_splits, o=o, workspace=ws)  # validates once
     import ctypes
     P = ctypes.c_void_p
+    heads = (Hq,) if Hq == H else (Hq, H)
     args = (P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), P(dt.data_ptr()),
-            P(dl.data_ptr()), P(o.data_ptr()), None, B, H, q_len, D, dk.shape[0], width, 16,
+            P(dl.data_ptr()), P(o.data_ptr()), None, B, *heads, q_len, D, dk.shape[0], width, 16,
             int(spec.causal), ctypes.c_float(spec.scale), spec.num_splits, P(ws.data_ptr()),
             ctypes.c_size_t(ws.numel() * 4), api.ATTN_BF16,
             P(torch.cuda.current_stream().cuda_stream))
-    fn = api.lib.attn_paged_decode
+    fn = api.lib.attn_paged_decode if Hq == H else api.lib.attn_paged_decode_gqa
 
     def call():
         if fn(*args) != 0:
-            raise RuntimeError("attn_paged_decode failed")
+            raise RuntimeError("paged decode failed")
 
     ms, wall = time_launches(torch, call, warmup, steps)
     # K and V bytes of every visible token, as the sequences address them
@@ -253,7 +257,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "copy"],
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "copy"],
                     help="run one workload and print its entry only")
     args = ap.parse_args()
 
@@ -269,7 +273,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import attention_tiled_qk_amd as api
-    from workloads import C2, C3, C4, C5
+    from workloads import C2, C3, C4, C4G, C5
 
     steps, warmup = args.steps, args.warmup
     runners = {
@@ -277,6 +281,7 @@ def main():
         "c3": lambda: bench_prefill(torch, api, C3, warmup, max(steps // 2, 3), "prefill_c3"),
         "c4": lambda: bench_paged(torch, api, C4, warmup, max(steps // 2, 3), "paged_c4"),
         "c5": lambda: bench_paged(torch, api, C5, warmup, max(steps // 2, 3), "paged_c5"),
+        "c4g": lambda: bench_paged(torch, api, C4G, warmup, max(steps // 2, 3), "paged_c4g"),
         "copy": lambda: bench_copy(torch, warmup, steps),
     }
     if args.only:
@@ -301,7 +306,7 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
-        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5")},
+        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g")},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")

@@ -139,6 +139,45 @@ int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                       void* stream);
 
 /*
+ * attn_paged_decode_gqa -- attn_paged_decode with grouped-query attention:
+ * Hq query heads share Hkv KV heads, query head hq reading KV head
+ * hq / (Hq / Hkv) (consecutive query heads form a group). The pools hold Hkv
+ * heads; one wave serves all Hq / Hkv query heads of a group from a single read
+ * of their K/V. [P3]'s item on cutting time-to-first-token names MQA and GQA
+ * (fewer KV heads than query heads) as the way to shrink the KV cache; this is
+ * that attention over the same paged cache. With Hq == Hkv it is
+ * attn_paged_decode.
+ *
+ *   q, o         : [B, Hq, q_len, D] bf16.
+ *   k_pool,
+ *   v_pool       : [num_blocks, Hkv, 16, D] bf16.
+ *   Hq, Hkv      : Hq a multiple of Hkv, and (Hq / Hkv) * q_len <= ATTN_PAGED_MAX_QLEN.
+ *   lse          : [B, Hq, q_len] float32 or NULL.
+ *   workspace    : at least attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D,
+ *                  max_blocks_per_seq, num_splits) bytes.
+ *   Every other argument, the masking and the split semantics are those of
+ *   attn_paged_decode. Returns ATTN_OK or a negative ATTN_ERR_* code
+ *   (ATTN_ERR_BAD_SHAPE when Hkv does not divide Hq, ATTN_ERR_UNSUPPORTED when
+ *   the group times q_len exceeds ATTN_PAGED_MAX_QLEN).
+ */
+int attn_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse,
+                          int B, int Hq, int Hkv, int q_len, int D, int num_blocks,
+                          int max_blocks_per_seq, int block_size, int causal, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, int dtype,
+                          void* stream);
+
+/*
+ * attn_paged_gqa_workspace_bytes -- split-KV scratch size for
+ * attn_paged_decode_gqa: 4 * B * Hq * q_len * S * (D + 1) bytes for the split
+ * count S it will use (num_splits, or its own choice for 0, which depends on
+ * B, Hkv and max_blocks_per_seq); 0 when one split suffices or the arguments
+ * are invalid.
+ */
+size_t attn_paged_gqa_workspace_bytes(int B, int Hq, int Hkv, int q_len, int D,
+                                      int max_blocks_per_seq, int num_splits);
+
+/*
  * attn_lse_merge -- the FlashDecoding cross-split reduction ([P3]): combine S
  * softmax-normalised partial outputs with their log-sum-exps. For each row,
  * M = max_p lse_p, w_p = exp(lse_p - M), o = sum_p w_p o_p / sum_p w_p and

@@ -184,14 +184,20 @@ def paged_gather(pool, block_tables, seq_lens, block_size=16):
 
 def paged_attention(q, k_pool, v_pool, block_tables, seq_lens, scale, causal,
                     block_size=16, heads=None):
-    """Attention of q [B, H, Lq, D] over each sequence's paged K/V.
+    """Attention of q [B, Hq, Lq, D] over each sequence's paged K/V.
 
     The key count of sequence b is seq_lens[b] and includes the Lq new tokens,
     so with ``causal`` query t sits at position seq_len - Lq + t (bottom-right).
-    Returns (o [B, H, Lq, D], lse [B, H, Lq]) in float64; with ``heads`` only
-    those (b, h) pairs are evaluated (others NaN).
+    The pools hold Hkv heads with Hq a multiple of Hkv; query head hq attends KV
+    head hq // (Hq // Hkv) (grouped-query attention; Hq == Hkv is ordinary
+    multi-head attention). Returns (o [B, Hq, Lq, D], lse [B, Hq, Lq]) in
+    float64; with ``heads`` only those (b, hq) pairs are evaluated (others NaN).
     """
     B, H, lq, D = q.shape
+    hkv = k_pool.shape[1]
+    if H % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = H // hkv
     o = np.full((B, H, lq, v_pool.shape[3]), np.nan)
     lse = np.full((B, H, lq), np.nan)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
@@ -204,7 +210,8 @@ def paged_attention(q, k_pool, v_pool, block_tables, seq_lens, scale, causal,
         for bb, h in pairs:
             if bb != b:
                 continue
-            o[b, h], lse[b, h] = dense_attention(q[b, h], kc[h], vc[h], scale, causal)
+            o[b, h], lse[b, h] = dense_attention(q[b, h], kc[h // group], vc[h // group], scale,
+                                                 causal)
     return o, lse
 
 

@@ -117,6 +117,28 @@ def test_paged_decode_rejects_bad_arguments(api):
     assert call(splits=4, ws=FAKE, ws_bytes=need - 4) == c["ATTN_ERR_WORKSPACE"]
 
 
+def test_paged_gqa_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+
+    def call(Hq=8, Hkv=2, q_len=1, splits=1, ws=None, ws_bytes=0, o=FAKE):
+        return L.attn_paged_decode_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, o, None, 2, Hq, Hkv, q_len, 128,
+                                       10, 8, 16, 1, 0.1, splits, ws, ws_bytes, 1, None)
+
+    assert call(Hq=6, Hkv=4) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(Hkv=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(Hq=34, Hkv=2, q_len=1) == c["ATTN_ERR_UNSUPPORTED"]  # 17 query columns > 16
+    assert call(Hq=16, Hkv=2, q_len=3) == c["ATTN_ERR_UNSUPPORTED"]  # 8 x 3 query columns > 16
+    assert call(o=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+    need = L.attn_paged_gqa_workspace_bytes(2, 8, 2, 1, 128, 8, 4)
+    assert need == 4 * 2 * 8 * 1 * 4 * (128 + 1)
+    assert call(splits=4) == c["ATTN_ERR_WORKSPACE"]
+    assert call(splits=4, ws=FAKE, ws_bytes=need - 4) == c["ATTN_ERR_WORKSPACE"]
+    assert L.attn_paged_gqa_workspace_bytes(2, 8, 3, 1, 128, 8, 4) == 0
+    # equal head counts reproduce the ungrouped size
+    assert L.attn_paged_gqa_workspace_bytes(2, 4, 4, 1, 128, 8, 4) == L.attn_paged_workspace_bytes(2, 4, 1, 128, 8, 4)
+
+
 def test_workspace_bytes(api):
     L = api.lib
     assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 16) == 4 * 4 * 40 * 5 * 16 * 129

@@ -273,6 +273,54 @@ def test_paged_other_scales(api, scale):
     assert max_err(o, ref_o) <= TOL_BF16 and lse_err(lse, ref_lse) <= TOL_LSE
 
 
+GQA_CASES = [(8, 1), (4, 4), (16, 1), (2, 5), (5, 3)]
+
+
+def _gqa_inputs(lens, q_len, hkv, group, seed):
+    inp = _paged(lens, q_len, H=hkv, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    q = torch.randn(len(lens), hkv * group, q_len, 128, generator=g).to(torch.bfloat16)
+    return PagedInputs(q, inp.k_pool, inp.v_pool, inp.block_tables, inp.seq_lens)
+
+
+@pytest.mark.parametrize("group,q_len", GQA_CASES)
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_paged_gqa(api, group, q_len, splits):
+    say(f"gqa group={group} q_len={q_len} splits={splits}")
+    inp = _gqa_inputs((q_len, 17, 100, 257, 1000), q_len, 2, group, seed=50 + group)
+    scale = 1.0 / math.sqrt(128)
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, scale, True)
+    o, lse = _run_paged(api, inp, splits)
+    e = max_err(o, ref_o)
+    say(f"  max|dO|={e:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= TOL_BF16 and lse_err(lse, ref_lse) <= TOL_LSE
+
+
+def test_paged_gqa_bit_identical_under_block_permutation(api):
+    inp = _gqa_inputs((5, 100, 257, 1000), 2, 2, 4, seed=60)
+    o1, l1 = _run_paged(api, inp, 3)
+    perm = permute_pool(inp, 4321)
+    o2, l2 = _run_paged(api, perm, 3)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_gqa_full_size_sampled(api):
+    from workloads import C4G
+    inp = paged_inputs(C4G)
+    lens = inp.seq_lens.tolist()
+    order = sorted(range(C4G.B), key=lambda b: lens[b])
+    pairs = [(b, h) for b in (order[0], order[-1], order[len(order) // 2]) for h in (0, 7, 8, 63)]
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, C4G.scale, True, heads=pairs)
+    o, lse = _run_paged(api, inp, C4G.num_splits, True, C4G.scale)
+    e = max_err(o, ref_o, pairs)
+    say(f"  gqa full size pairs={pairs} max|dO|={e:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= TOL_BF16 and lse_err(lse, ref_lse, pairs) <= TOL_LSE
+
+
 def test_paged_d64(api):
     inp = _paged((7, 70, 300), 5, D=64, seed=3)
     ref_o, _ = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,

@@ -336,6 +336,37 @@ def test_paged_full_query_equals_causal_prefill():
         np.testing.assert_allclose(lse[0, h], lb, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("group,q_len", [(2, 1), (4, 3), (8, 1)])
+def test_paged_gqa_equals_mha_on_repeated_kv_heads(group, q_len):
+    """Grouped-query attention is multi-head attention on a pool whose every KV
+    head is repeated for the query heads of its group."""
+    hkv = 2
+    inp = _small_paged(q_len=q_len, lens=(3, 17, 64, 100), H=hkv, D=8)
+    g = torch.Generator().manual_seed(7)
+    q = torch.randn(inp.q.shape[0], hkv * group, q_len, 8, generator=g).to(torch.bfloat16)
+    o, lse = oracle.paged_attention(q, inp.k_pool, inp.v_pool, inp.block_tables, inp.seq_lens,
+                                    0.3, True)
+    kr = inp.k_pool.repeat_interleave(group, dim=1)
+    vr = inp.v_pool.repeat_interleave(group, dim=1)
+    o2, l2 = oracle.paged_attention(q, kr, vr, inp.block_tables, inp.seq_lens, 0.3, True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # and one head against scalar loops: query head 2*group-1 reads KV head 1
+    kc = oracle.paged_gather(inp.k_pool, inp.block_tables, inp.seq_lens)
+    vc = oracle.paged_gather(inp.v_pool, inp.block_tables, inp.seq_lens)
+    hq = 2 * group - 1
+    ob, lb = brute_attention(q[2, hq].double().tolist(), kc[2][1].double().tolist(),
+                             vc[2][1].double().tolist(), 0.3, True)
+    np.testing.assert_allclose(o[2, hq], ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[2, hq], lb, rtol=0, atol=1e-12)
+
+
+def test_paged_gqa_rejects_uneven_heads():
+    inp = _small_paged(H=2, D=8)
+    q = torch.zeros(inp.q.shape[0], 3, 1, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        oracle.paged_attention(q, inp.k_pool, inp.v_pool, inp.block_tables, inp.seq_lens, 0.3, True)
+
+
 def test_paged_poison_never_read():
     spec = PagedSpec("p", 3, 2, 5, 16, 8, len_lo=5, len_hi=60, extra_blocks=4, poison=True)
     inp = paged_inputs(spec)

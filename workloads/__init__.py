@@ -58,6 +58,7 @@ class PagedSpec:
     causal: bool = True
     extra_blocks: int = 0
     poison: bool = False
+    q_heads: int = 0         # query heads when the pools hold fewer (grouped-query); 0 = H
 
     @property
     def scale(self):
@@ -79,7 +80,11 @@ C4 = PagedSpec("c4_paged_decode_bf16_64seq_40h_len128-4096", 64, 40, 1, 128, 4,
                len_lo=128, len_hi=4096)
 C5 = PagedSpec("c5_paged_verify_bf16_4seq_40h_q5_len32768_prefix2048_s16", 4, 40, 5, 128, 5,
                fixed_len=32768, shared_prefix_blocks=128, num_splits=16)
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+# Grouped-query decode (a follow-on of the paged path): 64 query heads reading 8
+# KV heads (group 8), the c4 length mix.
+C4G = PagedSpec("gqa_paged_decode_bf16_64seq_64qh_8kvh_len128-4096", 64, 8, 1, 128, 6,
+                len_lo=128, len_hi=4096, q_heads=64)
+CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c4g": C4G}
 
 
 def _randn(gen, shape, dtype):
@@ -138,7 +143,7 @@ def paged_inputs(spec):
     shape = (total, spec.H, BLOCK, spec.D)
     k_pool = _randn(g, shape, "bf16")
     v_pool = _randn(g, shape, "bf16")
-    q = _randn(g, (spec.B, spec.H, spec.q_len, spec.D), "bf16")
+    q = _randn(g, (spec.B, spec.q_heads or spec.H, spec.q_len, spec.D), "bf16")
     if spec.poison:
         _poison(k_pool, v_pool, lens, tables)
     return PagedInputs(q, k_pool, v_pool, tables, lens, perm)
