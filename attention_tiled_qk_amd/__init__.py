@@ -18,7 +18,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
-    "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes",
+    "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_prefill",
     "attn_lse_merge", "attn_paged_gather", "attn_version", "lib", "LIB_PATH",
     "ATTN_F32", "ATTN_BF16",
 ]
@@ -50,6 +50,9 @@ lib.attn_paged_gqa_workspace_bytes.restype = _sz
 lib.attn_paged_decode_gqa.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                                       _i, _f, _i, _p, _sz, _i, _p]
 lib.attn_paged_decode_gqa.restype = _i
+lib.attn_paged_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                   _f, _i, _p]
+lib.attn_paged_prefill.restype = _i
 lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
@@ -189,6 +192,41 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
     else:
         st = lib.attn_paged_decode_gqa(*common, Hq, Hkv, *tail)
         _check(st, "attn_paged_decode_gqa")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True, scale=None,
+                       o=None, lse=None, return_lse=False, stream=None):
+    """Chunked prefill over a paged cache: q [B, H, q_len, D] (bf16), the
+    q_len newest tokens of each sequence, attend its seq_lens[b] cached keys in
+    k_pool, v_pool [num_blocks, H, 16, D] through block_tables [B, W] int32."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [B, H, q_len, D] and the pools [num_blocks, H, 16, D]")
+    B, H, q_len, D = q.shape
+    nblk, Hp, bs, Dp = k_pool.shape
+    if Hp != H or Dp != D:
+        raise ValueError("pool heads / head_dim must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, q_len), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    st = lib.attn_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, q_len, D, nblk,
+                                block_tables.shape[1], bs, int(bool(causal)), float(scale),
+                                ATTN_BF16, _stream(q.device, stream))
+    _check(st, "attn_paged_prefill")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

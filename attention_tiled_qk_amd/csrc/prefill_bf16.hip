@@ -43,6 +43,7 @@ namespace attn {
 namespace {
 
 constexpr float kMaxTileSum = 1073741824.f;   // 2^30: bound on one lane's P sum per tile
+constexpr int kPagedMaxBlocks = 2048;         // cache blocks per sequence (32768 keys) in paged mode
 
 template <int D, int NW, int BN>
 struct PrefillCfg {
@@ -92,15 +93,27 @@ __device__ __forceinline__ void tile_of(int id, int n_heads, int n_qtiles, int& 
 
 }  // namespace
 
-template <int D, int NW, int BN, bool CAUSAL>
+// Where the keys come from when the kernel runs over a paged cache: the
+// queries are the q_len newest tokens of each sequence (chunked prefill), the
+// keys are its seq_lens[b] cached tokens read through its block table.
+struct PagedKV {
+  const int32_t* block_tables;  // [B, max_blocks]
+  const int32_t* seq_lens;      // [B], keys per sequence including the q_len new ones
+  int heads;                    // heads per sequence (pool and queries)
+  int max_blocks;
+};
+
+template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int L, int n_heads, int n_qtiles, float scale) {
+    bf16* __restrict__ o, float* __restrict__ lse, int L, int n_heads, int n_qtiles, float scale,
+    PagedKV pg) {
   using C = PrefillCfg<D, NW, BN>;
   __shared__ __attribute__((aligned(1024))) unsigned char ks0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char vs1[C::TILEB];
+  __shared__ int ids[PAGED ? kPagedMaxBlocks : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,25 +123,46 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   int bh, qt;
   tile_of(blockIdx.x, n_heads, n_qtiles, bh, qt);
-  const size_t head_off = (size_t)bh * L * D;
+  // L queries per head; Lk keys, the last L of which are the queries' own
+  // positions (Lk == L for dense prefill). Query row r sits at position off + r.
+  const size_t head_off = (size_t)bh * L * D;  // Q, O (and dense K, V) of this head
   const bf16* kh = k + head_off;
   const bf16* vh = v + head_off;
+  int Lk = L, hh = 0, seq = 0;
+  if constexpr (PAGED) {
+    seq = bh / pg.heads;
+    hh = bh - seq * pg.heads;
+    Lk = pg.seq_lens[seq];
+  }
+  const int off = Lk - L;
 
   const int q0 = qt * C::BM;
   const int wrow0 = q0 + wave * 32;
   const int my_row = wrow0 + l32;
-  const int n_kt = CAUSAL ? (min(q0 + C::BM, L) - 1) / BN + 1 : (L + BN - 1) / BN;
+  const int n_kt = CAUSAL ? (off + min(q0 + C::BM, L) - 1) / BN + 1 : (Lk + BN - 1) / BN;
   // last key tile holding a key that some row of this wave may see
-  const int last_w = CAUSAL ? min(n_kt - 1, (wrow0 + 31) / BN) : n_kt - 1;
+  const int last_w = CAUSAL ? min(n_kt - 1, (off + wrow0 + 31) / BN) : n_kt - 1;
 
+  // Per-lane source offsets of the tile loads: relative to the tile (dense) or
+  // to the piece's first row (paged: a piece's RPP rows are consecutive slots of
+  // one cache block, contiguous in the pool).
   unsigned koff[C::PPW], voff[C::PPW];
 #pragma unroll
   for (int i = 0; i < C::PPW; ++i) {
     const int piece = wave + NW * i;
     const int row = piece * C::RPP + lane / C::NCH;
     const int phys = lane % C::NCH;
-    koff[i] = row * C::ROWB + (phys ^ kswz<C::NCH>(row)) * 16;
-    voff[i] = row * C::ROWB + (phys ^ vswz<C::NCH>(row)) * 16;
+    const int base = PAGED ? (lane / C::NCH) * C::ROWB : row * C::ROWB;
+    koff[i] = base + (phys ^ kswz<C::NCH>(row)) * 16;
+    voff[i] = base + (phys ^ vswz<C::NCH>(row)) * 16;
+  }
+  if constexpr (PAGED) {
+    // stage this sequence's block ids once; reading them back from LDS keeps
+    // global loads (which complete in order) out of the prefetch pipeline
+    const int nb = min((Lk + 15) >> 4, pg.max_blocks);
+    const int32_t* tab = pg.block_tables + (size_t)seq * pg.max_blocks;
+    for (int i = tid; i < nb; i += NW * 64) ids[i] = tab[i];
+    __syncthreads();
   }
   auto kst = [&](auto s) -> ATTN_LDS unsigned char* {
     if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)ks0;
@@ -138,15 +172,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)vs0;
     else return (ATTN_LDS unsigned char*)vs1;
   };
+  // paged: the buffer range of piece i of tile kt -- the piece's rows inside
+  // their cache block, ending at the sequence's last key (rows past it, and
+  // pieces wholly past it, read as zeros)
+  auto paged_piece = [&](const bf16* pool, int kt, int i) -> __amdgpu_buffer_rsrc_t {
+    const int key = kt * BN + (wave + NW * i) * C::RPP;
+    if (key >= Lk) return buffer_rsrc(pool, 0);
+    const int blk = __builtin_amdgcn_readfirstlane(ids[key >> 4]);
+    const bf16* src = pool + (((size_t)blk * pg.heads + hh) * 16 + (key & 15)) * D;
+    return buffer_rsrc(src, min(C::RPP, Lk - key) * C::ROWB);
+  };
   auto issue_k = [&](auto s, int kt) {
-    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int i = 0; i < C::PPW; ++i) dma16(r, kst(s) + (wave + NW * i) * 1024, koff[i]);
+      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i), kst(s) + (wave + NW * i) * 1024, koff[i]);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
+#pragma unroll
+      for (int i = 0; i < C::PPW; ++i) dma16(r, kst(s) + (wave + NW * i) * 1024, koff[i]);
+    }
   };
   auto issue_v = [&](auto s, int kt) {
-    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int i = 0; i < C::PPW; ++i) dma16(r, vst(s) + (wave + NW * i) * 1024, voff[i]);
+      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i), vst(s) + (wave + NW * i) * 1024, voff[i]);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
+#pragma unroll
+      for (int i = 0; i < C::PPW; ++i) dma16(r, vst(s) + (wave + NW * i) * 1024, voff[i]);
+    }
   };
 
   int kaddr[C::KC];
@@ -207,9 +261,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   auto mask = [&](f32x16* sc, int kt) {
     const int key0 = kt * BN;
-    const bool need_mask = CAUSAL ? (key0 + BN - 1 > wrow0) : (key0 + BN > L);
+    const bool need_mask = CAUSAL ? (key0 + BN - 1 > off + wrow0) : (key0 + BN > Lk);
     if (need_mask) {
-      const int lim = (CAUSAL ? my_row : L - 1) - key0 - 4 * g;
+      const int lim = (CAUSAL ? off + my_row : Lk - 1) - key0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -358,21 +412,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-template <int D, int NW, int BN, bool CAUSAL>
+template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 hipError_t launch_prefill_pipe(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int L, float scale, hipStream_t stream) {
+                               int B, int H, int L, float scale, hipStream_t stream,
+                               PagedKV pg = PagedKV{nullptr, nullptr, 0, 0}) {
   using C = PrefillCfg<D, NW, BN>;
   const int n_qtiles = (L + C::BM - 1) / C::BM;
   const long long grid = (long long)B * H * n_qtiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_pipe_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_bf16_pipe_kernel<D, NW, BN, CAUSAL, PAGED>), dim3((unsigned)grid),
                      dim3(C::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                     (bf16*)o, lse, L, B * H, n_qtiles, scale);
+                     (bf16*)o, lse, L, B * H, n_qtiles, scale, pg);
   return hipGetLastError();
 }
 
 // Query rows per workgroup of the configuration launch_prefill_bf16 uses.
 int prefill_bf16_rows() { return 128; }
+
+// Longest sequence (in cache blocks) launch_paged_prefill_bf16 accepts.
+int paged_prefill_max_blocks() { return kPagedMaxBlocks; }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int L, int D, int causal, float scale,
@@ -383,6 +441,23 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   }
   return causal ? launch_prefill_pipe<64, 4, 64, true>(q, k, v, o, lse, B, H, L, scale, stream)
                 : launch_prefill_pipe<64, 4, 64, false>(q, k, v, o, lse, B, H, L, scale, stream);
+}
+
+hipError_t launch_paged_prefill_bf16(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                                     float* lse, int B, int H, int q_len, int D, int max_blocks,
+                                     int causal, float scale, hipStream_t stream) {
+  const PagedKV pg{block_tables, seq_lens, H, max_blocks};
+  if (D == 128) {
+    return causal ? launch_prefill_pipe<128, 4, 64, true, true>(q, k_pool, v_pool, o, lse, B, H,
+                                                                q_len, scale, stream, pg)
+                  : launch_prefill_pipe<128, 4, 64, false, true>(q, k_pool, v_pool, o, lse, B, H,
+                                                                 q_len, scale, stream, pg);
+  }
+  return causal ? launch_prefill_pipe<64, 4, 64, true, true>(q, k_pool, v_pool, o, lse, B, H, q_len,
+                                                             scale, stream, pg)
+                : launch_prefill_pipe<64, 4, 64, false, true>(q, k_pool, v_pool, o, lse, B, H, q_len,
+                                                              scale, stream, pg);
 }
 
 }  // namespace attn

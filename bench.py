@@ -17,11 +17,13 @@ The same run also measures, under ``secondary``:
     2048-token prefix, 16 splits merged by log-sum-exp;
   * c4g: grouped-query paged decode, 64 sequences, 64 query heads over 8 KV
     heads, q_len 1, lengths U[128, 4096];
+  * cpf: chunked prefill over the paged cache, 8 sequences x 40 heads, a
+    512-token chunk after a 3584-token cached prefix;
 each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
-``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, or ``copy``: a plain
+``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, cpf, or ``copy``: a plain
 device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
 its entry; that is the form the profiler runs use.
 
@@ -239,6 +241,57 @@ def bench_paged(torch, api, spec, warmup, steps, key):
     return res
 
 
+def bench_paged_prefill(torch, api, spec, warmup, steps, key):
+    import ctypes
+    from workloads import paged_inputs
+    log(f"[bench] building {spec.name} inputs")
+    inp = paged_inputs(spec)
+    dq, dk, dv, dt, dl = (t.cuda() for t in (inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                              inp.seq_lens))
+    B, H, q_len, D = inp.q.shape
+    o = torch.empty_like(dq)
+    api.attn_paged_prefill(dq, dk, dv, dt, dl, causal=spec.causal, scale=spec.scale, o=o)
+    P = ctypes.c_void_p
+    args = (P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), P(dt.data_ptr()),
+            P(dl.data_ptr()), P(o.data_ptr()), None, B, H, q_len, D, dk.shape[0],
+            inp.block_tables.shape[1], 16, int(spec.causal), ctypes.c_float(spec.scale),
+            api.ATTN_BF16, P(torch.cuda.current_stream().cuda_stream))
+    fn = api.lib.attn_paged_prefill
+
+    def call():
+        if fn(*args) != 0:
+            raise RuntimeError("attn_paged_prefill failed")
+
+    ms, wall = time_launches(torch, call, warmup, steps)
+    # visible (query, key) pairs: query t of a sequence of n keys sees n - q_len + t + 1
+    pairs = 0
+    for n in inp.seq_lens.tolist():
+        pairs += sum(n - q_len + t + 1 for t in range(q_len)) if spec.causal else n * q_len
+    flops = 4.0 * D * H * pairs
+    achieved = flops / (ms * 1e-3) / 1e12
+    traffic = load_traffic(key, source_digest(*KERNEL_SOURCES["prefill"]))
+    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/launch, {achieved:.0f} TFLOP/s "
+        f"({achieved / PEAK_BF16_TFLOPS:.1%} of peak)")
+    del dq, dk, dv, dt, dl, o
+    torch.cuda.empty_cache()
+    return {
+        "workload": spec.name,
+        "ms_per_step": wall / steps,
+        "value": flops / (wall / steps * 1e-3) / 1e12,
+        "roofline": {
+            "kernel": f"prefill_bf16_pipe_kernel<{D}, paged>",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": flops,
+            "launch_us_events": ms * 1e3,
+        },
+    }
+
+
 def bench_copy(torch, warmup, steps):
     """Plain 2 GiB device copy: the calibration kernel for HBM byte counters."""
     n = 1 << 31
@@ -257,7 +310,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "copy"],
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "cpf", "copy"],
                     help="run one workload and print its entry only")
     args = ap.parse_args()
 
@@ -273,7 +326,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import attention_tiled_qk_amd as api
-    from workloads import C2, C3, C4, C4G, C5
+    from workloads import C2, C3, C4, C4G, C5, CPF
 
     steps, warmup = args.steps, args.warmup
     runners = {
@@ -282,6 +335,7 @@ def main():
         "c4": lambda: bench_paged(torch, api, C4, warmup, max(steps // 2, 3), "paged_c4"),
         "c5": lambda: bench_paged(torch, api, C5, warmup, max(steps // 2, 3), "paged_c5"),
         "c4g": lambda: bench_paged(torch, api, C4G, warmup, max(steps // 2, 3), "paged_c4g"),
+        "cpf": lambda: bench_paged_prefill(torch, api, CPF, warmup, max(steps // 2, 3), "prefill_cpf"),
         "copy": lambda: bench_copy(torch, warmup, steps),
     }
     if args.only:
@@ -306,7 +360,7 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
-        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g")},
+        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g", "cpf")},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")

@@ -138,6 +138,37 @@ int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                       int num_splits, void* workspace, size_t workspace_bytes, int dtype,
                       void* stream);
 
+/* Longest sequence attn_paged_prefill accepts, in 16-token blocks (32768 keys). */
+#define ATTN_PAGED_PREFILL_MAX_BLOCKS 2048
+
+/*
+ * attn_paged_prefill -- chunked prefill over a PagedAttention cache: the q_len
+ * newest tokens of each sequence (already written to the cache) attend all of
+ * its seq_lens[b] cached keys, read through its block table. This is the step
+ * that splits a long prompt into chunks interleaved with decode ([P3], the
+ * chunked-prefill and TTFT items), with the cache layout of [P1] §3.2; it runs
+ * the tiled online-softmax prefill kernel with its K/V tiles gathered block by
+ * block from the pool.
+ *
+ *   q, o         : [B, H, q_len, D] bf16 (query t of sequence b is its token
+ *                  seq_lens[b] - q_len + t).
+ *   k_pool,
+ *   v_pool       : [num_blocks, H, 16, D] bf16.
+ *   block_tables : [B, max_blocks_per_seq] int32 device; entries past
+ *                  ceil(seq_lens[b] / 16) are never read.
+ *   seq_lens     : [B] int32 device, q_len <= seq_lens[b] <= max_blocks_per_seq * 16.
+ *   lse          : [B, H, q_len] float32 or NULL.
+ *   D            : 64 or 128; block_size must be 16;
+ *   max_blocks_per_seq <= ATTN_PAGED_PREFILL_MAX_BLOCKS.
+ *   causal       : bottom-right (query t sees keys 0 .. seq_lens[b] - q_len + t).
+ * Slots past seq_lens[b] are never read. Returns ATTN_OK or a negative
+ * ATTN_ERR_* code.
+ */
+int attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse,
+                       int B, int H, int q_len, int D, int num_blocks, int max_blocks_per_seq,
+                       int block_size, int causal, float scale, int dtype, void* stream);
+
 /*
  * attn_paged_decode_gqa -- attn_paged_decode with grouped-query attention:
  * Hq query heads share Hkv KV heads, query head hq reading KV head

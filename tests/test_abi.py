@@ -139,6 +139,27 @@ def test_paged_gqa_rejects_bad_arguments(api):
     assert L.attn_paged_gqa_workspace_bytes(2, 4, 4, 1, 128, 8, 4) == L.attn_paged_workspace_bytes(2, 4, 1, 128, 8, 4)
 
 
+def test_paged_prefill_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+
+    def call(q=FAKE, o=FAKE, B=2, H=4, q_len=64, D=128, nblk=10, width=8, bs=16, causal=1,
+             scale=0.1, dtype=1):
+        return L.attn_paged_prefill(q, FAKE, FAKE, FAKE, FAKE, o, None, B, H, q_len, D, nblk,
+                                    width, bs, causal, scale, dtype, None)
+
+    assert call(q=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(q_len=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(q_len=8 * 16 + 1) == c["ATTN_ERR_BAD_SHAPE"]  # longer than the table can hold
+    assert call(dtype=0) == c["ATTN_ERR_BAD_DTYPE"]
+    assert call(D=96) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(bs=8) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(width=2049) == c["ATTN_ERR_UNSUPPORTED"]  # ATTN_PAGED_PREFILL_MAX_BLOCKS + 1
+    assert call(causal=2) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(scale=float("inf")) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(o=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+
+
 def test_workspace_bytes(api):
     L = api.lib
     assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 16) == 4 * 4 * 40 * 5 * 16 * 129

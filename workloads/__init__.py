@@ -84,7 +84,11 @@ C5 = PagedSpec("c5_paged_verify_bf16_4seq_40h_q5_len32768_prefix2048_s16", 4, 40
 # KV heads (group 8), the c4 length mix.
 C4G = PagedSpec("gqa_paged_decode_bf16_64seq_64qh_8kvh_len128-4096", 64, 8, 1, 128, 6,
                 len_lo=128, len_hi=4096, q_heads=64)
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c4g": C4G}
+# Chunked prefill over the paged cache (a follow-on of the paged path): 8
+# sequences x 40 heads, a 512-token chunk after a 3584-token cached prefix.
+CPF = PagedSpec("chunked_prefill_bf16_8seq_40h_chunk512_len4096", 8, 40, 512, 128, 7,
+                fixed_len=4096)
+CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c4g": C4G, "cpf": CPF}
 
 
 def _randn(gen, shape, dtype):
