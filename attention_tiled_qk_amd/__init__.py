@@ -19,8 +19,8 @@ from .build import LIB_PATH
 __all__ = [
     "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
     "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_prefill",
-    "attn_lse_merge", "attn_paged_gather", "attn_version", "lib", "LIB_PATH",
-    "ATTN_F32", "ATTN_BF16",
+    "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
+    "KVCacheAllocator", "attn_version", "lib", "LIB_PATH", "ATTN_F32", "ATTN_BF16",
 ]
 
 ATTN_F32 = 0
@@ -57,6 +57,28 @@ lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_gather.restype = _i
+lib.attn_paged_append.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
+lib.attn_paged_append.restype = _i
+lib.attn_paged_copy_blocks.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+lib.attn_paged_copy_blocks.restype = _i
+lib.attn_kv_cache_create.argtypes = [_i, _i, _i]
+lib.attn_kv_cache_create.restype = _p
+lib.attn_kv_cache_destroy.argtypes = [_p]
+lib.attn_kv_cache_destroy.restype = None
+lib.attn_kv_cache_append.argtypes = [_p, _i, _i, _p, _p, _i, ctypes.POINTER(_i)]
+lib.attn_kv_cache_append.restype = _i
+lib.attn_kv_cache_fork.argtypes = [_p, _i, _i]
+lib.attn_kv_cache_fork.restype = _i
+lib.attn_kv_cache_release.argtypes = [_p, _i]
+lib.attn_kv_cache_release.restype = _i
+lib.attn_kv_cache_length.argtypes = [_p, _i]
+lib.attn_kv_cache_length.restype = _i
+lib.attn_kv_cache_free_blocks.argtypes = [_p]
+lib.attn_kv_cache_free_blocks.restype = _i
+lib.attn_kv_cache_block_refs.argtypes = [_p, _i]
+lib.attn_kv_cache_block_refs.restype = _i
+lib.attn_kv_cache_export.argtypes = [_p, _p, _p]
+lib.attn_kv_cache_export.restype = _i
 lib.attn_status_string.argtypes = [_i]
 lib.attn_status_string.restype = ctypes.c_char_p
 lib.attn_version.argtypes = []
@@ -266,3 +288,106 @@ def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, st
                                nblk, width, max_seq_len, _stream(pool.device, stream))
     _check(st, "attn_paged_gather")
     return out
+
+
+def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, stream=None):
+    """Write k_new, v_new [B, H, n_new, D] (bf16) into the pools [N, H, 16, D]
+    in place: token t of sequence b goes to position seq_lens[b] - n_new + t
+    (seq_lens counts the new tokens) through block_tables [B, W] int32."""
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or k_pool.dim() != 4 \
+            or v_pool.shape != k_pool.shape:
+        raise ValueError("k_new, v_new must be [B, H, n_new, D] and the pools [N, H, 16, D]")
+    B, H, n_new, D = k_new.shape
+    nblk, Hp, bs, Dp = k_pool.shape
+    if Hp != H or Dp != D:
+        raise ValueError("pool heads / head_dim must match the new tokens")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    st = lib.attn_paged_append(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(block_tables), _ptr(seq_lens), B, H, n_new, D, nblk,
+                               block_tables.shape[1], bs, ATTN_BF16,
+                               _stream(k_new.device, stream))
+    _check(st, "attn_paged_append")
+
+
+def attn_paged_copy_blocks(k_pool, v_pool, src, dst, *, stream=None):
+    """Copy physical block src[i] onto dst[i] in both pools (int32 device ids)."""
+    _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16)
+    _dev(src, "src", torch.int32)
+    _dev(dst, "dst", torch.int32)
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or src.dim() != 1 \
+            or dst.shape != src.shape:
+        raise ValueError("pools must be [N, H, 16, D] and src, dst 1-D of one length")
+    nblk, H, _, D = k_pool.shape
+    st = lib.attn_paged_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst),
+                                    src.numel(), nblk, H, D, ATTN_BF16,
+                                    _stream(k_pool.device, stream))
+    _check(st, "attn_paged_copy_blocks")
+
+
+class KVCacheAllocator:
+    """Host block allocator of a paged cache (the attn_kv_cache_* calls).
+
+    Blocks are taken as sequences grow and returned on release; fork shares a
+    sequence's blocks by reference count, and append reports the one block
+    copy that copy-on-write needs as a (src, dst) pair.
+    """
+
+    def __init__(self, num_blocks, max_seqs, max_blocks_per_seq):
+        self.num_blocks = num_blocks
+        self.max_seqs = max_seqs
+        self.max_blocks_per_seq = max_blocks_per_seq
+        self._destroy = lib.attn_kv_cache_destroy  # kept for interpreter shutdown
+        self._h = lib.attn_kv_cache_create(num_blocks, max_seqs, max_blocks_per_seq)
+        if not self._h:
+            raise ValueError("attn_kv_cache_create failed: sizes must be positive")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def append(self, seq, n_tokens):
+        """Reserve n_tokens more tokens for seq; returns the copies [(src, dst)]."""
+        src = (ctypes.c_int32 * 1)()
+        dst = (ctypes.c_int32 * 1)()
+        n = _i(0)
+        _check(lib.attn_kv_cache_append(self._h, seq, n_tokens, src, dst, 1, ctypes.byref(n)),
+               "attn_kv_cache_append")
+        return [(src[0], dst[0])] if n.value else []
+
+    def fork(self, parent, child):
+        _check(lib.attn_kv_cache_fork(self._h, parent, child), "attn_kv_cache_fork")
+
+    def release(self, seq):
+        _check(lib.attn_kv_cache_release(self._h, seq), "attn_kv_cache_release")
+
+    def length(self, seq):
+        r = lib.attn_kv_cache_length(self._h, seq)
+        _check(min(r, 0), "attn_kv_cache_length")
+        return r
+
+    def free_blocks(self):
+        return lib.attn_kv_cache_free_blocks(self._h)
+
+    def refs(self, block):
+        r = lib.attn_kv_cache_block_refs(self._h, block)
+        _check(min(r, 0), "attn_kv_cache_block_refs")
+        return r
+
+    def export(self):
+        """(block_tables [max_seqs, max_blocks_per_seq], seq_lens [max_seqs]) int32 CPU tensors."""
+        tables = torch.empty((self.max_seqs, self.max_blocks_per_seq), dtype=torch.int32)
+        lens = torch.empty((self.max_seqs,), dtype=torch.int32)
+        _check(lib.attn_kv_cache_export(self._h, _ptr(tables), _ptr(lens)), "attn_kv_cache_export")
+        return tables, lens

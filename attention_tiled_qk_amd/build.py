@@ -21,7 +21,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "paged.hip"]
+SOURCES = [
+    "attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "paged.hip", "kv_append.hip",
+    "kv_cache.hip",
+]
 
 
 def _hipcc():

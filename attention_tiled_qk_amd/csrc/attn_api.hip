@@ -26,6 +26,10 @@ hipError_t launch_lse_merge(const float*, const float*, void*, float*, long long
                             hipStream_t);
 hipError_t launch_paged_gather(const void*, const int32_t*, const int32_t*, void*, int, int, int,
                                int, int, hipStream_t);
+hipError_t launch_paged_append(const void*, const void*, void*, void*, const int32_t*,
+                               const int32_t*, int, int, int, int, int, hipStream_t);
+hipError_t launch_paged_copy_blocks(void*, void*, const int32_t*, const int32_t*, int, int, int,
+                                    hipStream_t);
 }  // namespace attn
 
 namespace {
@@ -91,6 +95,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_OVERFLOW: return "sizes overflow the kernels' indexing";
     case ATTN_ERR_HIP: return "kernel launch failed";
+    case ATTN_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
     default: return "unknown status";
   }
 }
@@ -275,6 +280,45 @@ int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32
   return hip_status(attn::launch_paged_gather(pool, block_tables, seq_lens, out, B, H, D,
                                               max_blocks_per_seq, max_seq_len,
                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, int B, int H,
+                      int n_new, int D, int num_blocks, int max_blocks_per_seq, int block_size,
+                      int dtype, void* stream) {
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens)
+    return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || n_new <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != ATTN_BLOCK_SIZE) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)n_new > (long long)max_blocks_per_seq * 16) return ATTN_ERR_BAD_SHAPE;
+  if (H > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({B, H, n_new, D, 2}) < 0 || checked_mul({num_blocks, H, 16, D, 2}) < 0 ||
+      checked_mul({B, max_blocks_per_seq}) < 0)
+    return ATTN_ERR_OVERFLOW;
+  if (((long long)n_new * (D / 8) + 255) / 256 > kMaxGrid) return ATTN_ERR_OVERFLOW;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return ATTN_ERR_MISALIGNED;
+  if (!aligned4(block_tables) || !aligned4(seq_lens)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_paged_append(k_new, v_new, k_pool, v_pool, block_tables,
+                                              seq_lens, B, H, n_new, D, max_blocks_per_seq,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                           int n, int num_blocks, int H, int D, int dtype, void* stream) {
+  if (!k_pool || !v_pool || !src || !dst) return ATTN_ERR_NULL_PTR;
+  if (n <= 0 || num_blocks <= 0 || H <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (n > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({num_blocks, H, 16, D, 2}) < 0) return ATTN_ERR_OVERFLOW;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_MISALIGNED;
+  if (!aligned4(src) || !aligned4(dst)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_paged_copy_blocks(k_pool, v_pool, src, dst, n, H, D,
+                                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -19,11 +19,13 @@ The same run also measures, under ``secondary``:
     heads, q_len 1, lengths U[128, 4096];
   * cpf: chunked prefill over the paged cache, 8 sequences x 40 heads, a
     512-token chunk after a 3584-token cached prefix;
+  * append: writing that 512-token chunk's K and V into the paged pools
+    (attn_paged_append), priced against HBM bandwidth;
 each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
-``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, cpf, or ``copy``: a plain
+``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, cpf, append, or ``copy``: a plain
 device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
 its entry; that is the form the profiler runs use.
 
@@ -63,6 +65,7 @@ def source_digest(*names):
 KERNEL_SOURCES = {
     "prefill": ("prefill_bf16.hip", "common.h"),
     "paged": ("paged.hip", "common.h"),
+    "append": ("kv_append.hip", "common.h"),
 }
 
 
@@ -292,6 +295,55 @@ def bench_paged_prefill(torch, api, spec, warmup, steps, key):
     }
 
 
+def bench_append(torch, api, spec, warmup, steps, key):
+    """K/V of one q_len-token chunk per sequence written into the pools."""
+    import ctypes
+    from workloads import paged_layout
+    log(f"[bench] building append inputs for {spec.name}")
+    lens, tables, total, _ = paged_layout(spec)
+    B, H, n_new, D = spec.B, spec.H, spec.q_len, spec.D
+    g = torch.Generator(device="cuda").manual_seed(spec.seed)
+    k_new = torch.randn((B, H, n_new, D), device="cuda", generator=g).to(torch.bfloat16)
+    v_new = torch.randn((B, H, n_new, D), device="cuda", generator=g).to(torch.bfloat16)
+    k_pool = torch.zeros((total, H, 16, D), device="cuda", dtype=torch.bfloat16)
+    v_pool = torch.zeros_like(k_pool)
+    dt, dl = tables.cuda(), lens.cuda()
+    api.attn_paged_append(k_new, v_new, k_pool, v_pool, dt, dl)  # validates once
+    P = ctypes.c_void_p
+    args = (P(k_new.data_ptr()), P(v_new.data_ptr()), P(k_pool.data_ptr()), P(v_pool.data_ptr()),
+            P(dt.data_ptr()), P(dl.data_ptr()), B, H, n_new, D, total, tables.shape[1], 16,
+            api.ATTN_BF16, P(torch.cuda.current_stream().cuda_stream))
+    fn = api.lib.attn_paged_append
+
+    def call():
+        if fn(*args) != 0:
+            raise RuntimeError("attn_paged_append failed")
+
+    ms, wall = time_launches(torch, call, warmup, steps)
+    moved = 2.0 * 2 * B * H * n_new * D * 2  # K and V: read once, written once
+    gbs = moved / (ms * 1e-3) / 1e9
+    log(f"[bench] append {spec.name}: {ms * 1e3:.1f} us/launch, {gbs:.0f} GB/s "
+        f"({gbs / PEAK_HBM_GBS:.1%})")
+    del k_new, v_new, k_pool, v_pool, dt, dl
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"kv_append_bf16_{B}seq_{H}h_{n_new}tok_d{D}",
+        "ms_per_step": wall / steps,
+        "value": moved / (wall / steps * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": f"paged_append_kernel<{D}>",
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": load_traffic(key, source_digest(*KERNEL_SOURCES["append"])),
+            "algorithmic_bytes_per_launch": moved,
+            "launch_us_events": ms * 1e3,
+        },
+    }
+
+
 def bench_copy(torch, warmup, steps):
     """Plain 2 GiB device copy: the calibration kernel for HBM byte counters."""
     n = 1 << 31
@@ -310,7 +362,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "cpf", "copy"],
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "cpf", "append", "copy"],
                     help="run one workload and print its entry only")
     args = ap.parse_args()
 
@@ -336,6 +388,7 @@ def main():
         "c5": lambda: bench_paged(torch, api, C5, warmup, max(steps // 2, 3), "paged_c5"),
         "c4g": lambda: bench_paged(torch, api, C4G, warmup, max(steps // 2, 3), "paged_c4g"),
         "cpf": lambda: bench_paged_prefill(torch, api, CPF, warmup, max(steps // 2, 3), "prefill_cpf"),
+        "append": lambda: bench_append(torch, api, CPF, warmup, max(steps // 2, 3), "append_cpf"),
         "copy": lambda: bench_copy(torch, warmup, steps),
     }
     if args.only:
@@ -360,7 +413,7 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
-        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g", "cpf")},
+        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g", "cpf", "append")},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")

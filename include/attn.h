@@ -14,7 +14,12 @@
  *        the FlashAttention-2 item, the FlashDecoding item (split the key range
  *        across workgroups, then a cross-split reduction kernel), and the
  *        Continuous Batching + PagedAttention item (the kernel receives each
- *        request's block table and reads only valid blocks).
+ *        request's block table and reads only valid blocks; blocks are
+ *        allocated as a request grows and freed when it ends).
+ *   [P4] fanzheng.org inference survey, section on KV-cache runtime
+ *        management and reuse, subsection on paged memory management:
+ *        physical blocks carry reference counts, sequences that share them
+ *        copy on write.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
@@ -58,7 +63,8 @@ enum attn_status {
   ATTN_ERR_MISALIGNED = -5,  /* a pointer is not 16-byte aligned */
   ATTN_ERR_WORKSPACE = -6,   /* workspace missing or smaller than attn_paged_workspace_bytes() */
   ATTN_ERR_OVERFLOW = -7,    /* an element count does not fit the kernels' 32/64-bit indexing */
-  ATTN_ERR_HIP = -8          /* the kernel launch itself failed (hipGetLastError) */
+  ATTN_ERR_HIP = -8,         /* the kernel launch itself failed (hipGetLastError) */
+  ATTN_ERR_NO_BLOCKS = -9    /* the block allocator has too few free blocks */
 };
 
 /* Largest query count per sequence accepted by attn_paged_decode. */
@@ -242,6 +248,102 @@ int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* l
 int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32_t* seq_lens,
                       void* out, int B, int H, int D, int num_blocks, int max_blocks_per_seq,
                       int max_seq_len, void* stream);
+
+/*
+ * attn_paged_append -- write n_new new tokens of K and V per sequence into the
+ * paged pools ([P1] §3.2 layout; [P3] Continuous Batching + PagedAttention:
+ * the cache grows block by block). Token t of sequence b has position
+ * p = seq_lens[b] - n_new + t and lands in physical block
+ * block_tables[b][p / 16], slot p % 16 -- the exact inverse of the gather that
+ * the attention calls perform. Bit-exact copy.
+ *
+ *   k_new, v_new : [B, H, n_new, D] bf16, contiguous.
+ *   k_pool,
+ *   v_pool       : [num_blocks, H, 16, D] bf16, written in place.
+ *   block_tables : [B, max_blocks_per_seq] int32 device; the blocks covering
+ *                  the new positions must already be assigned (see the
+ *                  allocator below).
+ *   seq_lens     : [B] int32 device, lengths INCLUDING the new tokens. A
+ *                  sequence with seq_lens[b] < n_new places only the tokens
+ *                  whose position is >= 0; table entries < 0 are skipped.
+ *   D            : 64 or 128; block_size must be 16.
+ * Sequences must not share a destination block (copy a shared block first,
+ * attn_paged_copy_blocks). Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, int B, int H,
+                      int n_new, int D, int num_blocks, int max_blocks_per_seq, int block_size,
+                      int dtype, void* stream);
+
+/*
+ * attn_paged_copy_blocks -- copy-on-write support ([P4]): copy physical block
+ * src[i] onto dst[i] (all H heads, all 16 slots) in both pools, for i < n.
+ * Bit-exact. src and dst are int32 device arrays of n block ids in
+ * [0, num_blocks); no dst may appear twice or also appear in src.
+ *   k_pool, v_pool : [num_blocks, H, 16, D] bf16.  D: 64 or 128.  n <= 65535.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                           int n, int num_blocks, int H, int D, int dtype, void* stream);
+
+/*
+ * Host block allocator of the paged cache ([P3] Continuous Batching +
+ * PagedAttention: blocks are taken as a sequence grows and returned when it
+ * ends; [P4] paged memory management: reference-counted blocks, shared by
+ * forked sequences, copied on write; [P1] §3.2 and [P2] §二: requests with a
+ * common prefix share its blocks).
+ *
+ * Pure host bookkeeping, no device memory and no HIP calls. A handle is not
+ * thread-safe: one caller at a time. Physical ids run 0 .. num_blocks - 1 and
+ * the lowest free id is handed out first on a fresh pool.
+ */
+typedef struct attn_kv_cache attn_kv_cache;
+
+/* New allocator with every block free and max_seqs empty sequences, each
+ * holding at most max_blocks_per_seq blocks. NULL on a non-positive size or
+ * out of host memory. */
+attn_kv_cache* attn_kv_cache_create(int num_blocks, int max_seqs, int max_blocks_per_seq);
+
+/* Free the handle (NULL is accepted). */
+void attn_kv_cache_destroy(attn_kv_cache* cache);
+
+/*
+ * Reserve room for n_tokens more tokens of sequence `seq`: new blocks are taken
+ * when the last one is full. When the last block is only partly filled and is
+ * shared with another sequence (reference count > 1), the sequence gets a
+ * private copy: a fresh block replaces it in the table and the pair
+ * (shared, fresh) is written to copy_src[0], copy_dst[0] with *n_copies = 1;
+ * the caller must copy those blocks on the device (attn_paged_copy_blocks)
+ * before writing the new tokens. Otherwise *n_copies = 0.
+ * Errors leave the allocator unchanged: ATTN_ERR_NO_BLOCKS when the free
+ * blocks do not suffice, ATTN_ERR_BAD_SHAPE for a bad seq, negative n_tokens
+ * or a length past max_blocks_per_seq * 16, ATTN_ERR_WORKSPACE when a copy is
+ * needed but max_copies < 1 or the copy arrays are NULL.
+ */
+int attn_kv_cache_append(attn_kv_cache* cache, int seq, int n_tokens, int32_t* copy_src,
+                         int32_t* copy_dst, int max_copies, int* n_copies);
+
+/* Make empty sequence `child` share all blocks of `parent` (reference counts
+ * +1), with the same length. ATTN_ERR_BAD_SHAPE if child is not empty. */
+int attn_kv_cache_fork(attn_kv_cache* cache, int parent, int child);
+
+/* Drop sequence `seq`: its blocks' reference counts go down by one and blocks
+ * that reach 0 return to the free pool. The sequence becomes empty. */
+int attn_kv_cache_release(attn_kv_cache* cache, int seq);
+
+/* Tokens held by `seq`, or a negative ATTN_ERR_* code. */
+int attn_kv_cache_length(const attn_kv_cache* cache, int seq);
+
+/* Number of free blocks, or a negative ATTN_ERR_* code. */
+int attn_kv_cache_free_blocks(const attn_kv_cache* cache);
+
+/* Reference count of physical block `block`, or a negative ATTN_ERR_* code. */
+int attn_kv_cache_block_refs(const attn_kv_cache* cache, int block);
+
+/* Write the tables to HOST arrays: block_tables [max_seqs, max_blocks_per_seq]
+ * int32 (unused entries -1) and seq_lens [max_seqs] int32, ready to copy to the
+ * device for the attention and append calls. */
+int attn_kv_cache_export(const attn_kv_cache* cache, int32_t* block_tables, int32_t* seq_lens);
 
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_string(int status);

@@ -17,7 +17,8 @@ Sources (the web pages this library follows; sections as they appear there):
        idea, FlashAttention-2, FlashDecoding, and Continuous Batching with
        PagedAttention (block tables passed to the kernel).
   [P4] fanzheng.org, "a survey of advances in LLM since the transformer:
-       inference" -- roofline, MFU/MBU, PagedAttention (16-token blocks).
+       inference" -- roofline, MFU/MBU, PagedAttention (16-token blocks,
+       reference-counted physical blocks copied on write).
 
 Every function here is pinned by tests that do not re-run its own formula
 (brute-force scalar loops, a library routine, closed forms, invariants and a
@@ -36,3 +37,4 @@ from .attention import (  # noqa: F401
     split_partials,
     lse_merge,
 )
+from .cache import paged_append, copy_blocks  # noqa: F401,E402

@@ -192,3 +192,36 @@ def test_binding_refuses_cpu_tensors(api):
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         api.attn_prefill(x, x, x)
+
+
+def test_append_and_copy_reject_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+    ok = dict(B=2, H=4, n=3, D=128, nb=16, W=4, bs=16, dtype=1)
+
+    def app(k_new=FAKE, v_new=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, **kw):
+        a = dict(ok, **kw)
+        return L.attn_paged_append(k_new, v_new, kp, vp, bt, sl, a["B"], a["H"], a["n"], a["D"],
+                                   a["nb"], a["W"], a["bs"], a["dtype"], None)
+
+    assert app(k_new=None) == c["ATTN_ERR_NULL_PTR"]
+    assert app(sl=None) == c["ATTN_ERR_NULL_PTR"]
+    assert app(n=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert app(B=-1) == c["ATTN_ERR_BAD_SHAPE"]
+    assert app(n=4 * 16 + 1) == c["ATTN_ERR_BAD_SHAPE"]  # more new tokens than a table can hold
+    assert app(dtype=0) == c["ATTN_ERR_BAD_DTYPE"]
+    assert app(D=96) == c["ATTN_ERR_UNSUPPORTED"]
+    assert app(bs=32) == c["ATTN_ERR_UNSUPPORTED"]
+    assert app(H=70000) == c["ATTN_ERR_OVERFLOW"]
+    assert app(B=60000, H=60000, n=1 << 30, W=1 << 27) == c["ATTN_ERR_OVERFLOW"]
+    assert app(kp=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+
+    def cp(kp=FAKE, vp=FAKE, s=FAKE, d=FAKE, n=2, nb=16, H=4, D=128, dtype=1):
+        return L.attn_paged_copy_blocks(kp, vp, s, d, n, nb, H, D, dtype, None)
+
+    assert cp(s=None) == c["ATTN_ERR_NULL_PTR"]
+    assert cp(n=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert cp(dtype=0) == c["ATTN_ERR_BAD_DTYPE"]
+    assert cp(D=32) == c["ATTN_ERR_UNSUPPORTED"]
+    assert cp(n=70000) == c["ATTN_ERR_OVERFLOW"]
+    assert cp(vp=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]

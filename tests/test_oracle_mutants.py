@@ -217,3 +217,71 @@ def test_split_mutant_caught(bug):
 
     assert not _fails_some([run(None)], None)
     assert _fails_some([run(bug)], None)
+
+
+def _append_variant(k_pool, v_pool, block_tables, seq_lens, k_new, v_new, block_size=16,
+                    bug=None):
+    tables = np.asarray(block_tables, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    n_new = k_new.shape[2]
+    for b in range(tables.shape[0]):
+        for t in range(n_new):
+            p = int(lens[b]) + t if bug == "position_after_len" else int(lens[b]) - n_new + t
+            if p < 0 or (bug == "first_token_dropped" and t == 0):
+                continue
+            blk = p % block_size if bug == "slot_block_swapped" else p // block_size
+            phys = blk if bug == "logical_not_physical" else int(tables[b][blk])
+            if phys < 0 or phys >= k_out.shape[0]:
+                continue
+            slot = p // block_size if bug == "slot_block_swapped" else p % block_size
+            slot = min(slot, block_size - 1)
+            k_out[phys, :, slot, :] = k_new[b, :, t, :]
+            v_out[phys, :, slot, :] = (k_new if bug == "k_for_v" else v_new)[b, :, t, :]
+    return k_out, v_out
+
+
+APPEND_BUGS = ["position_after_len", "first_token_dropped", "slot_block_swapped",
+               "logical_not_physical", "k_for_v"]
+
+
+@pytest.mark.parametrize("bug", APPEND_BUGS)
+def test_append_mutant_caught(bug, monkeypatch):
+    from tests import test_kv_cache as pins
+
+    def variant(*a, **kw):
+        return _append_variant(*a, bug=bug, **kw)
+
+    monkeypatch.setattr(oracle, "paged_append", variant)
+    checks = [pins.test_append_places_tokens_as_the_paging_figure_draws_them,
+              pins.test_append_then_gather_round_trip,
+              pins.test_append_in_pieces_equals_append_at_once,
+              pins.test_append_skips_negative_positions]
+    caught = 0
+    for chk in checks:
+        try:
+            chk()
+        except (AssertionError, IndexError, ValueError):
+            caught += 1
+    assert caught > 0
+
+
+def _copy_variant(k_pool, v_pool, src, dst, bug=None):
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    for s, d in zip(src, dst):
+        if bug == "reversed":
+            s, d = d, s
+        k_out[int(d)] = k_pool[int(s)]
+        if bug != "k_only":
+            v_out[int(d)] = v_pool[int(s)]
+    return k_out, v_out
+
+
+@pytest.mark.parametrize("bug", ["reversed", "k_only"])
+def test_copy_mutant_caught(bug, monkeypatch):
+    from tests import test_kv_cache as pins
+    monkeypatch.setattr(oracle, "copy_blocks", lambda *a: _copy_variant(*a, bug=bug))
+    with pytest.raises(AssertionError):
+        pins.test_copy_blocks_preserves_what_a_rewritten_table_reads()
