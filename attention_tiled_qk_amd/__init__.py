@@ -19,6 +19,7 @@ from .build import LIB_PATH
 __all__ = [
     "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
     "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_prefill",
+    "attn_paged_prefill_varlen",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
     "KVCacheAllocator", "attn_version", "lib", "LIB_PATH", "ATTN_F32", "ATTN_BF16",
 ]
@@ -53,6 +54,9 @@ lib.attn_paged_decode_gqa.restype = _i
 lib.attn_paged_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                                    _f, _i, _p]
 lib.attn_paged_prefill.restype = _i
+lib.attn_paged_prefill_varlen.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                          _i, _i, _i, _f, _i, _p]
+lib.attn_paged_prefill_varlen.restype = _i
 lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
@@ -249,6 +253,46 @@ def attn_paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True
                                 block_tables.shape[1], bs, int(bool(causal)), float(scale),
                                 ATTN_BF16, _stream(q.device, stream))
     _check(st, "attn_paged_prefill")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_lens, max_q_len, *,
+                              causal=True, scale=None, o=None, lse=None, return_lse=False,
+                              stream=None):
+    """Ragged chunked prefill over a paged cache: q [total_q, H, D] (bf16,
+    token-major), sequence b owning query tokens cu_q_lens[b] .. cu_q_lens[b+1]-1
+    (int32 device, B + 1 entries); ``max_q_len`` is the largest of those counts.
+    Returns o [total_q, H, D] (and lse [total_q, H] float32)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_pool, "k_pool", torch.bfloat16)
+    _dev(v_pool, "v_pool", torch.bfloat16)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(cu_q_lens, "cu_q_lens", torch.int32)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [total_q, H, D] and the pools [num_blocks, H, 16, D]")
+    total_q, H, D = q.shape
+    nblk, Hp, bs, Dp = k_pool.shape
+    if Hp != H or Dp != D:
+        raise ValueError("pool heads / head_dim must match q")
+    B = seq_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or cu_q_lens.shape != (B + 1,):
+        raise ValueError("block_tables must be [B, W], seq_lens [B] and cu_q_lens [B + 1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, H), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    st = lib.attn_paged_prefill_varlen(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                       _ptr(seq_lens), _ptr(cu_q_lens), _ptr(o), _ptr(lse), B, H,
+                                       total_q, int(max_q_len), D, nblk, block_tables.shape[1],
+                                       bs, int(bool(causal)), float(scale), ATTN_BF16,
+                                       _stream(q.device, stream))
+    _check(st, "attn_paged_prefill_varlen")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

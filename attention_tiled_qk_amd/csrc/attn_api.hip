@@ -15,7 +15,7 @@ hipError_t launch_prefill_bf16(const void*, const void*, const void*, void*, flo
                                int, int, float, hipStream_t);
 hipError_t launch_paged_prefill_bf16(const void*, const void*, const void*, const int32_t*,
                                      const int32_t*, void*, float*, int, int, int, int, int, int,
-                                     float, hipStream_t);
+                                     float, hipStream_t, const int32_t*);
 int paged_prefill_max_blocks();
 hipError_t launch_prefill_f32(const void*, const void*, const void*, void*, float*, int, int, int,
                               int, int, float, hipStream_t);
@@ -219,7 +219,43 @@ int attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
   return hip_status(attn::launch_paged_prefill_bf16(q, k_pool, v_pool, block_tables, seq_lens, o,
                                                     lse, B, H, q_len, D, max_blocks_per_seq,
                                                     causal, scale,
-                                                    reinterpret_cast<hipStream_t>(stream)));
+                                                    reinterpret_cast<hipStream_t>(stream), nullptr));
+}
+
+int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* cu_q_lens, void* o, float* lse, int B, int H,
+                              int total_q, int max_q_len, int D, int num_blocks,
+                              int max_blocks_per_seq, int block_size, int causal, float scale,
+                              int dtype, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !cu_q_lens || !o)
+    return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || total_q <= 0 || max_q_len <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (max_q_len > total_q) return ATTN_ERR_BAD_SHAPE;
+  if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != ATTN_BLOCK_SIZE) return ATTN_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq > attn::paged_prefill_max_blocks()) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_q_len > (long long)max_blocks_per_seq * 16) return ATTN_ERR_BAD_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+  if (checked_mul({num_blocks, H, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
+      checked_mul({total_q, H, D, 4}) < 0)
+    return ATTN_ERR_OVERFLOW;
+  if ((long long)B * H * ((max_q_len + kPrefillRowsBf16 - 1) / kPrefillRowsBf16) > kMaxGrid)
+    return ATTN_ERR_OVERFLOW;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
+    return ATTN_ERR_MISALIGNED;
+  if (!aligned4(block_tables) || !aligned4(seq_lens) || !aligned4(cu_q_lens) ||
+      (lse && !aligned4(lse)))
+    return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_paged_prefill_bf16(q, k_pool, v_pool, block_tables, seq_lens, o,
+                                                    lse, B, H, max_q_len, D, max_blocks_per_seq,
+                                                    causal, scale,
+                                                    reinterpret_cast<hipStream_t>(stream),
+                                                    cu_q_lens));
 }
 
 size_t attn_paged_gqa_workspace_bytes(int B, int Hq, int Hkv, int q_len, int D,

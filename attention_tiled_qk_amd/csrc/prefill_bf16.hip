@@ -95,10 +95,14 @@ __device__ __forceinline__ void tile_of(int id, int n_heads, int n_qtiles, int& 
 
 // Where the keys come from when the kernel runs over a paged cache: the
 // queries are the q_len newest tokens of each sequence (chunked prefill), the
-// keys are its seq_lens[b] cached tokens read through its block table.
+// keys are its seq_lens[b] cached tokens read through its block table. With
+// cu_q set, sequences have their own query counts (a ragged batch): sequence b
+// owns packed query tokens cu_q[b] .. cu_q[b+1]-1, and q, o and lse are laid
+// out token-major ([total_q, heads, D] and [total_q, heads]).
 struct PagedKV {
   const int32_t* block_tables;  // [B, max_blocks]
-  const int32_t* seq_lens;      // [B], keys per sequence including the q_len new ones
+  const int32_t* seq_lens;      // [B], keys per sequence including its new tokens
+  const int32_t* cu_q;          // [B + 1] packed query offsets, or null (q_len = L for all)
   int heads;                    // heads per sequence (pool and queries)
   int max_blocks;
 };
@@ -125,14 +129,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   tile_of(blockIdx.x, n_heads, n_qtiles, bh, qt);
   // L queries per head; Lk keys, the last L of which are the queries' own
   // positions (Lk == L for dense prefill). Query row r sits at position off + r.
-  const size_t head_off = (size_t)bh * L * D;  // Q, O (and dense K, V) of this head
+  const size_t head_off = (size_t)bh * L * D;  // dense K, V of this head
   const bf16* kh = k + head_off;
   const bf16* vh = v + head_off;
+  size_t qo_off = head_off;       // Q, O row 0 of this head
+  size_t row_stride = D;          // elements between consecutive query rows
+  size_t lse_off = (size_t)bh * L;
+  size_t lse_stride = 1;
   int Lk = L, hh = 0, seq = 0;
   if constexpr (PAGED) {
     seq = bh / pg.heads;
     hh = bh - seq * pg.heads;
     Lk = pg.seq_lens[seq];
+    if (pg.cu_q != nullptr) {
+      const int c0 = pg.cu_q[seq];
+      L = pg.cu_q[seq + 1] - c0;
+      if (qt * C::BM >= L) return;  // whole workgroup: past this sequence's queries
+      qo_off = ((size_t)c0 * pg.heads + hh) * D;
+      row_stride = (size_t)pg.heads * D;
+      lse_off = (size_t)c0 * pg.heads + hh;
+      lse_stride = pg.heads;
+    }
   }
   const int off = Lk - L;
 
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   bf16x8 qreg[C::KC];
   {
     const bool ok = my_row < L;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + head_off + (size_t)(ok ? my_row : 0) * D + 8 * g);
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + qo_off + (ok ? my_row : 0) * row_stride + 8 * g);
     const unsigned flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) {
@@ -396,7 +413,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const float l_tot = sum_xor32(l_run);
   if (my_row < L) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = o + head_off + (size_t)my_row * D;
+    bf16* orow = o + qo_off + my_row * row_stride;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -408,14 +425,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         *reinterpret_cast<u32x2*>(orow + d) = w;
       }
     if (lse != nullptr && g == 0)
-      lse[(size_t)bh * L + my_row] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
+      lse[lse_off + my_row * lse_stride] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
   }
 }
 
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 hipError_t launch_prefill_pipe(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int L, float scale, hipStream_t stream,
-                               PagedKV pg = PagedKV{nullptr, nullptr, 0, 0}) {
+                               PagedKV pg = PagedKV{nullptr, nullptr, nullptr, 0, 0}) {
   using C = PrefillCfg<D, NW, BN>;
   const int n_qtiles = (L + C::BM - 1) / C::BM;
   const long long grid = (long long)B * H * n_qtiles;
@@ -446,8 +463,10 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
 hipError_t launch_paged_prefill_bf16(const void* q, const void* k_pool, const void* v_pool,
                                      const int32_t* block_tables, const int32_t* seq_lens, void* o,
                                      float* lse, int B, int H, int q_len, int D, int max_blocks,
-                                     int causal, float scale, hipStream_t stream) {
-  const PagedKV pg{block_tables, seq_lens, H, max_blocks};
+                                     int causal, float scale, hipStream_t stream,
+                                     const int32_t* cu_q) {
+  // with cu_q, q_len is the longest sequence's query count (it sizes the grid)
+  const PagedKV pg{block_tables, seq_lens, cu_q, H, max_blocks};
   if (D == 128) {
     return causal ? launch_prefill_pipe<128, 4, 64, true, true>(q, k_pool, v_pool, o, lse, B, H,
                                                                 q_len, scale, stream, pg)

@@ -176,6 +176,32 @@ int attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
                        int block_size, int causal, float scale, int dtype, void* stream);
 
 /*
+ * attn_paged_prefill_varlen -- attn_paged_prefill for a ragged batch: each
+ * sequence brings its own number of new query tokens, the way continuous
+ * batching packs prompt chunks of different lengths (and single decode
+ * tokens) into one step ([P3], the chunked-prefill and continuous-batching
+ * items). Sequence b owns packed query tokens cu_q_lens[b] .. cu_q_lens[b+1]-1;
+ * its t-th new token sits at position seq_lens[b] - q_len_b + t.
+ *
+ *   q, o         : [total_q, H, D] bf16, token-major (token i, head h at
+ *                  (i * H + h) * D).
+ *   lse          : [total_q, H] float32, or NULL.
+ *   cu_q_lens    : [B + 1] int32 device, cu_q_lens[0] = 0, non-decreasing,
+ *                  cu_q_lens[B] = total_q; q_len_b = cu_q_lens[b+1] - cu_q_lens[b]
+ *                  may be 0 and must not exceed max_q_len or seq_lens[b]
+ *                  (device contents are trusted, as for block tables).
+ *   max_q_len    : the largest q_len_b (sizes the launch), <= total_q.
+ *   Pools, tables, seq_lens, D, block_size, causal and scale as for
+ *   attn_paged_prefill. Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* cu_q_lens, void* o, float* lse, int B, int H,
+                              int total_q, int max_q_len, int D, int num_blocks,
+                              int max_blocks_per_seq, int block_size, int causal, float scale,
+                              int dtype, void* stream);
+
+/*
  * attn_paged_decode_gqa -- attn_paged_decode with grouped-query attention:
  * Hq query heads share Hkv KV heads, query head hq reading KV head
  * hq / (Hq / Hkv) (consecutive query heads form a group). The pools hold Hkv

@@ -33,6 +33,7 @@ from .attention import (  # noqa: F401
     online_softmax_attention,
     paged_gather,
     paged_attention,
+    paged_attention_varlen,
     split_ranges,
     split_partials,
     lse_merge,

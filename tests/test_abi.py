@@ -225,3 +225,27 @@ def test_append_and_copy_reject_bad_arguments(api):
     assert cp(D=32) == c["ATTN_ERR_UNSUPPORTED"]
     assert cp(n=70000) == c["ATTN_ERR_OVERFLOW"]
     assert cp(vp=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+
+
+def test_paged_prefill_varlen_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+    ok = dict(B=2, H=4, total=40, maxq=30, D=128, nb=64, W=8, bs=16, causal=1, dtype=1)
+
+    def call(q=FAKE, cu=FAKE, o=FAKE, **kw):
+        a = dict(ok, **kw)
+        return L.attn_paged_prefill_varlen(q, FAKE, FAKE, FAKE, FAKE, cu, o, None, a["B"], a["H"],
+                                           a["total"], a["maxq"], a["D"], a["nb"], a["W"],
+                                           a["bs"], a["causal"], 0.1, a["dtype"], None)
+
+    assert call(cu=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(o=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(total=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(maxq=41) == c["ATTN_ERR_BAD_SHAPE"]          # longer than all queries together
+    assert call(maxq=200, total=400) == c["ATTN_ERR_BAD_SHAPE"]  # past the table's 128 keys
+    assert call(causal=2) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(dtype=0) == c["ATTN_ERR_BAD_DTYPE"]
+    assert call(D=80) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(W=2049) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(cu=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
+    assert call(q=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]

@@ -388,6 +388,72 @@ def test_paged_prefill_full_size_sampled(api):
     assert e <= TOL_BF16 and lse_err(lse, ref_lse, pairs) <= TOL_LSE
 
 
+def _run_varlen(api, inp, qlens, q, causal=True, scale=None):
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32)
+    D = q.shape[2]
+    scale = scale if scale is not None else 1.0 / math.sqrt(D)
+    dq, dk, dv, dt, dl, dc = to_dev(q, inp.k_pool, inp.v_pool, inp.block_tables, inp.seq_lens, cu)
+    o, lse = api.attn_paged_prefill_varlen(dq, dk, dv, dt, dl, dc, max(qlens), causal=causal,
+                                           scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse, cu
+
+
+VARLEN_CASES = [
+    ((300, 1000, 2500, 64, 700), (300, 1, 130, 0, 700), 128),
+    ((16, 17, 4097, 33), (16, 2, 257, 33), 64),
+]
+
+
+@pytest.mark.parametrize("lens,qlens,D", VARLEN_CASES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_prefill_varlen(api, lens, qlens, D, causal):
+    say(f"varlen prefill lens={lens} qlens={qlens} D={D} causal={causal}")
+    inp = _paged(lens, 1, H=3, D=D, seed=90 + D)
+    g = torch.Generator().manual_seed(91)
+    q = torch.randn(sum(qlens), 3, D, generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    o, lse, cu = _run_varlen(api, inp, qlens, q, causal, scale)
+    ref_o, ref_lse = oracle.paged_attention_varlen(q, cu, inp.k_pool, inp.v_pool,
+                                                   inp.block_tables, inp.seq_lens, scale, causal)
+    e = max_err(o, ref_o)
+    el = lse_err(lse, ref_lse)
+    say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert torch.isfinite(o.float()).all()
+    assert e <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_paged_prefill_varlen_equal_lengths_bit_identical(api):
+    """Equal query counts: the ragged call gives attn_paged_prefill's bits."""
+    inp = _paged((300, 1000, 200), 200, H=2, seed=92)
+    o1, l1 = _run_paged_prefill(api, inp)
+    B, H, lq, D = inp.q.shape
+    packed = inp.q.permute(0, 2, 1, 3).contiguous().reshape(B * lq, H, D)
+    o2, l2, _ = _run_varlen(api, inp, [lq] * B, packed)
+    assert torch.equal(o2.reshape(B, lq, H, D).permute(0, 2, 1, 3), o1)
+    assert torch.equal(l2.reshape(B, lq, H).permute(0, 2, 1), l1)
+
+
+def test_paged_prefill_varlen_mixed_batch_full_size(api):
+    """A continuous-batching step at the 13B shape: 4 sequences bring a
+    512-token prompt chunk and 4 bring one decode token, 40 heads, 4096 cached
+    keys each; sampled sequences against the oracle."""
+    from workloads import CPF
+    inp = paged_inputs(CPF)
+    qlens = [512, 1, 512, 1, 512, 1, 512, 1]
+    g = torch.Generator().manual_seed(93)
+    q = torch.randn(sum(qlens), CPF.H, CPF.D, generator=g).to(torch.bfloat16)
+    o, lse, cu = _run_varlen(api, inp, qlens, q, True, CPF.scale)
+    ref_o, ref_lse = oracle.paged_attention_varlen(q, cu, inp.k_pool, inp.v_pool,
+                                                   inp.block_tables, inp.seq_lens, CPF.scale,
+                                                   True, seqs=[1, 6])
+    rows = [r for b in (1, 6) for r in range(int(cu[b]), int(cu[b + 1]))]
+    e = float(np.abs(o.double().cpu().numpy()[rows] - ref_o[rows]).max())
+    el = float(np.abs(lse.double().cpu().numpy()[rows] - ref_lse[rows]).max())
+    say(f"  mixed batch max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_LSE
+
+
 def test_paged_d64(api):
     inp = _paged((7, 70, 300), 5, D=64, seed=3)
     ref_o, _ = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,

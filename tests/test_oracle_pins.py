@@ -360,6 +360,42 @@ def test_paged_gqa_equals_mha_on_repeated_kv_heads(group, q_len):
     np.testing.assert_allclose(lse[2, hq], lb, rtol=0, atol=1e-12)
 
 
+def test_paged_varlen_equal_lengths_is_paged_attention():
+    """With every sequence bringing q_len tokens, the ragged form is
+    paged_attention on the token-major repacking of q."""
+    inp = _small_paged(q_len=4, lens=(5, 17, 64, 100), H=3, D=8)
+    B, H, lq, D = inp.q.shape
+    packed = inp.q.permute(0, 2, 1, 3).reshape(B * lq, H, D)
+    cu = torch.arange(0, B * lq + 1, lq, dtype=torch.int32)
+    o, lse = oracle.paged_attention_varlen(packed, cu, inp.k_pool, inp.v_pool, inp.block_tables,
+                                           inp.seq_lens, 0.3, True)
+    o2, l2 = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                    inp.seq_lens, 0.3, True)
+    assert np.array_equal(o, o2.transpose(0, 2, 1, 3).reshape(B * lq, H, D))
+    assert np.array_equal(lse, l2.transpose(0, 2, 1).reshape(B * lq, H))
+
+
+def test_paged_varlen_ragged_against_scalar_loops():
+    """Query counts 3, 0, 1, 9: each sequence's rows against brute force."""
+    inp = _small_paged(q_len=1, lens=(20, 33, 7, 50), H=2, D=8)
+    qlens = [3, 0, 1, 9]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32)
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(int(cu[-1]), 2, 8, generator=g).to(torch.bfloat16)
+    o, lse = oracle.paged_attention_varlen(q, cu, inp.k_pool, inp.v_pool, inp.block_tables,
+                                           inp.seq_lens, 0.5, True)
+    assert np.all(np.isfinite(o)) and o.shape == (13, 2, 8)
+    kc = oracle.paged_gather(inp.k_pool, inp.block_tables, inp.seq_lens)
+    vc = oracle.paged_gather(inp.v_pool, inp.block_tables, inp.seq_lens)
+    for b in (0, 2, 3):
+        a, e = int(cu[b]), int(cu[b + 1])
+        for h in range(2):
+            ob, lb = brute_attention(q[a:e, h].double().tolist(), kc[b][h].double().tolist(),
+                                     vc[b][h].double().tolist(), 0.5, True)
+            np.testing.assert_allclose(o[a:e, h], ob, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[a:e, h], lb, rtol=0, atol=1e-12)
+
+
 def test_paged_gqa_rejects_uneven_heads():
     inp = _small_paged(H=2, D=8)
     q = torch.zeros(inp.q.shape[0], 3, 1, 8, dtype=torch.bfloat16)
