@@ -39,3 +39,11 @@ from .attention import (  # noqa: F401
     lse_merge,
 )
 from .cache import paged_append, copy_blocks  # noqa: F401,E402
+from .fp8 import (  # noqa: F401,E402
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_append,
+    dequantize,
+    paged_attention_fp8,
+)

@@ -285,3 +285,116 @@ def test_copy_mutant_caught(bug, monkeypatch):
     monkeypatch.setattr(oracle, "copy_blocks", lambda *a: _copy_variant(*a, bug=bug))
     with pytest.raises(AssertionError):
         pins.test_copy_blocks_preserves_what_a_rewritten_table_reads()
+
+
+# ------------------------------------------------------------------ fp8 ---
+
+def _encode_variant(x, bug):
+    from oracle import fp8 as f
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x.astype(np.float64))
+    if bug != "no_clamp":
+        a = np.minimum(a, f.E4M3_MAX)
+    hi = np.minimum(np.searchsorted(f._POS_VALS, a, side="left"), len(f._POS_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - f._POS_VALS[lo]
+    d_hi = f._POS_VALS[hi] - a
+    if bug == "ties_away":
+        pick_hi = d_hi <= d_lo
+    elif bug == "truncate":
+        pick_hi = d_hi == 0
+    else:
+        pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (f._POS_CODES[hi] % 2 == 0))
+    if bug == "no_clamp":
+        pick_hi = pick_hi | (a > f.E4M3_MAX)
+        mag = np.where(a > f.E4M3_MAX, 0x7F, np.where(pick_hi, f._POS_CODES[hi], f._POS_CODES[lo]))
+    else:
+        mag = np.where(pick_hi, f._POS_CODES[hi], f._POS_CODES[lo])
+    return (mag | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("bug", ["ties_away", "truncate", "no_clamp"])
+def test_fp8_encode_mutant_caught(bug, monkeypatch):
+    from oracle import fp8 as f
+    from tests import test_fp8_oracle as pins
+    var = lambda x: _encode_variant(x, bug)  # noqa: E731
+    monkeypatch.setattr(oracle, "e4m3_encode", var)
+    monkeypatch.setattr(f, "e4m3_encode", var)
+    checks = [pins.test_encode_matches_library_on_values_and_ties,
+              pins.test_encode_clamps_out_of_range,
+              pins.test_append_fresh_blocks_error_bound_and_max_code]
+    caught = 0
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            caught += 1
+    assert caught > 0
+
+
+def _append_fp8_variant(bug):
+    from oracle import fp8 as f
+
+    def run(k_codes, k_scale, v_codes, v_scale, block_tables, seq_lens, k_new, v_new,
+            block_size=16):
+        tables = np.asarray(block_tables, dtype=np.int64)
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        out = []
+        for codes, scale, new in ((k_codes, k_scale, k_new), (v_codes, v_scale, v_new)):
+            c = np.array(codes, dtype=np.uint8, copy=True)
+            s = np.array(scale, dtype=np.float32, copy=True)
+            x = np.asarray(new, dtype=np.float32)
+            n_new = x.shape[2]
+            for b in range(tables.shape[0]):
+                first = max(int(lens[b]) - n_new, 0)
+                last = int(lens[b])
+                p = first
+                while p < last:
+                    lb = p // block_size
+                    s0 = p - lb * block_size
+                    s1 = min(last - lb * block_size, block_size)
+                    phys = int(tables[b][lb])
+                    t0 = lb * block_size + s0 - (int(lens[b]) - n_new)
+                    for h in range(c.shape[1]):
+                        vals = x[b, h, t0:t0 + (s1 - s0)]
+                        amax = np.float32(np.max(np.abs(vals)))
+                        s_old = np.float32(0) if (s0 == 0 and bug != "stale_scale") else s[phys, h]
+                        cand = np.float32(amax / np.float32(448))
+                        s_new = cand if bug == "scale_shrinks" else max(s_old, cand)
+                        if s_new > s_old and s0 > 0 and bug != "no_reencode":
+                            old = f.e4m3_decode(c[phys, h, :s0]).astype(np.float32)
+                            c[phys, h, :s0] = f.e4m3_encode((old * s_old) / s_new)
+                        c[phys, h, s0:s1] = f.e4m3_encode(vals / s_new) if s_new > 0 else 0
+                        s[phys, h] = s_new
+                    p = lb * block_size + s1
+            out += [c, s]
+        return tuple(out)
+    return run
+
+
+@pytest.mark.parametrize("bug", ["stale_scale", "scale_shrinks", "no_reencode"])
+def test_fp8_append_mutant_caught(bug, monkeypatch):
+    from tests import test_fp8_oracle as pins
+    monkeypatch.setattr(oracle, "quantize_append", _append_fp8_variant(bug))
+    checks = [pins.test_append_fresh_blocks_error_bound_and_max_code,
+              pins.test_append_exact_on_representable_values,
+              pins.test_append_in_pieces_equals_at_once_while_scale_stands,
+              pins.test_append_growing_scale_reencodes_old_slots,
+              pins.test_append_at_slot_zero_ignores_a_stale_scale,
+              pins.test_append_all_zero_block_has_zero_scale]
+    caught = 0
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            caught += 1
+    assert caught > 0
+
+
+def test_fp8_append_variant_without_bug_passes(monkeypatch):
+    """The mutant harness itself: with no planted bug every pin passes."""
+    from tests import test_fp8_oracle as pins
+    monkeypatch.setattr(oracle, "quantize_append", _append_fp8_variant(None))
+    pins.test_append_fresh_blocks_error_bound_and_max_code()
+    pins.test_append_growing_scale_reencodes_old_slots()
+    pins.test_append_at_slot_zero_ignores_a_stale_scale()
