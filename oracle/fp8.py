@@ -100,7 +100,8 @@ def quantize_append(k_codes, k_scale, v_codes, v_scale, block_tables, seq_lens, 
     k_codes, v_codes [num_blocks, H, block_size, D] uint8; k_scale, v_scale
     [num_blocks, H] float32; k_new, v_new [B, H, n_new, D] (any float dtype,
     finite). Token t of sequence b sits at position seq_lens[b] - n_new + t
-    (seq_lens count the new tokens); negative positions are skipped. Each
+    (seq_lens count the new tokens); negative positions, and blocks whose
+    table entry is negative, are skipped. Each
     (block, head) that receives tokens follows the scale rule of the module
     docstring.
     """
@@ -123,6 +124,9 @@ def quantize_append(k_codes, k_scale, v_codes, v_scale, block_tables, seq_lens, 
                 s1 = min(last - lb * block_size, block_size)
                 phys = int(tables[b][lb])
                 t0 = lb * block_size + s0 - (int(lens[b]) - n_new)
+                p = lb * block_size + s1
+                if phys < 0:  # no block assigned: nothing is placed
+                    continue
                 for h in range(H):
                     vals = x[b, h, t0:t0 + (s1 - s0)]                     # [n, D] float32
                     amax = np.float32(np.max(np.abs(vals))) if vals.size else np.float32(0)
@@ -136,7 +140,6 @@ def quantize_append(k_codes, k_scale, v_codes, v_scale, block_tables, seq_lens, 
                     else:
                         c[phys, h, s0:s1] = 0
                     s[phys, h] = s_new
-                p = lb * block_size + s1
         out += [c, s]
     return tuple(out)
 

@@ -157,6 +157,19 @@ def test_append_at_slot_zero_ignores_a_stale_scale():
     np.testing.assert_allclose(oracle.dequantize(c2, s2)[1, 0, 0], x[0, 0, 0], rtol=2.0 ** -4)
 
 
+def test_append_skips_unassigned_blocks():
+    """A table entry of -1 places nothing (and must not wrap to the last block)."""
+    kc, ks = _cache(3, 1, 4)
+    x = np.ones((1, 1, 6, 4), dtype=np.float32)
+    c2, s2, _, _ = oracle.quantize_append(kc, ks, kc, ks, [[1, -1]], [20], x, x)
+    assert np.array_equal(c2[2], kc[2]) and s2[2, 0] == ks[2, 0]
+    assert np.array_equal(c2[0], kc[0])
+    # block 1 got slots 14, 15 over its stored scale, which already covers them
+    assert s2[1, 0] == max(ks[1, 0], np.float32(1) / np.float32(448))
+    assert np.array_equal(c2[1, 0, :14], kc[1, 0, :14])
+    assert (c2[1, 0, 14:] == oracle.e4m3_encode(np.float32(1) / s2[1, 0])).all()
+
+
 def test_append_all_zero_block_has_zero_scale():
     kc, ks = _cache(1, 1, 4)
     z = np.zeros((1, 1, 3, 4), dtype=np.float32)
