@@ -21,7 +21,8 @@ __all__ = [
     "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_prefill",
     "attn_paged_prefill_varlen",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
-    "KVCacheAllocator", "attn_version", "lib", "LIB_PATH", "ATTN_F32", "ATTN_BF16",
+    "KVCacheAllocator", "attn_paged_append_fp8", "attn_paged_copy_blocks_fp8",
+    "attn_paged_decode_fp8", "attn_version", "lib", "LIB_PATH", "ATTN_F32", "ATTN_BF16",
 ]
 
 ATTN_F32 = 0
@@ -65,6 +66,14 @@ lib.attn_paged_append.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i
 lib.attn_paged_append.restype = _i
 lib.attn_paged_copy_blocks.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_copy_blocks.restype = _i
+lib.attn_paged_append_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                      _p]
+lib.attn_paged_append_fp8.restype = _i
+lib.attn_paged_copy_blocks_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p]
+lib.attn_paged_copy_blocks_fp8.restype = _i
+lib.attn_paged_decode_fp8.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                      _i, _i, _i, _f, _i, _p, _sz, _p]
+lib.attn_paged_decode_fp8.restype = _i
 lib.attn_kv_cache_create.argtypes = [_i, _i, _i]
 lib.attn_kv_cache_create.restype = _p
 lib.attn_kv_cache_destroy.argtypes = [_p]
@@ -374,6 +383,92 @@ def attn_paged_copy_blocks(k_pool, v_pool, src, dst, *, stream=None):
                                     src.numel(), nblk, H, D, ATTN_BF16,
                                     _stream(k_pool.device, stream))
     _check(st, "attn_paged_copy_blocks")
+
+
+def _fp8_pools(k_pool, v_pool, k_scale, v_scale):
+    _dev(k_pool, "k_pool", torch.uint8)
+    _dev(v_pool, "v_pool", torch.uint8)
+    _dev(k_scale, "k_scale", torch.float32)
+    _dev(v_scale, "v_scale", torch.float32)
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("FP8 pools must be uint8 [num_blocks, H, 16, D]")
+    if k_scale.shape != k_pool.shape[:2] or v_scale.shape != k_scale.shape:
+        raise ValueError("scales must be float32 [num_blocks, H]")
+    return k_pool.shape
+
+
+def attn_paged_append_fp8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables,
+                          seq_lens, *, stream=None):
+    """Quantise k_new, v_new [B, H, n_new, D] (bf16) into FP8 pools (uint8
+    E4M3 codes [N, H, 16, D] with float32 scales [N, H]), in place."""
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    nblk, H, bs, D = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if k_new.dim() != 4 or v_new.shape != k_new.shape or k_new.shape[1] != H \
+            or k_new.shape[3] != D:
+        raise ValueError("k_new, v_new must be [B, H, n_new, D] matching the pools")
+    B, _, n_new, _ = k_new.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    st = lib.attn_paged_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                   _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                   _ptr(seq_lens), B, H, n_new, D, nblk, block_tables.shape[1],
+                                   bs, _stream(k_new.device, stream))
+    _check(st, "attn_paged_append_fp8")
+
+
+def attn_paged_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src, dst, *, stream=None):
+    """Copy FP8 block src[i] (codes and scales) onto dst[i] in both pools."""
+    nblk, H, _, D = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(src, "src", torch.int32)
+    _dev(dst, "dst", torch.int32)
+    if src.dim() != 1 or dst.shape != src.shape:
+        raise ValueError("src, dst must be 1-D of one length")
+    st = lib.attn_paged_copy_blocks_fp8(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                        _ptr(src), _ptr(dst), src.numel(), nblk, H, D,
+                                        _stream(k_pool.device, stream))
+    _check(st, "attn_paged_copy_blocks_fp8")
+
+
+def attn_paged_decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, *,
+                          causal=True, scale=None, num_splits=0, o=None, lse=None,
+                          return_lse=False, workspace=None, stream=None):
+    """Attention of q [B, Hq, q_len, D] (bf16) over FP8 pools (uint8 E4M3
+    [N, Hkv, 16, D], float32 scales [N, Hkv]); Hkv divides Hq."""
+    _dev(q, "q", torch.bfloat16)
+    nblk, Hkv, bs, Dp = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Hq, q_len, D]")
+    B, Hq, q_len, D = q.shape
+    if Dp != D or Hq % Hkv != 0:
+        raise ValueError("pool head_dim must match q and pool heads must divide query heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    width = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, q_len), device=q.device, dtype=torch.float32)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    need = attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, width, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.attn_paged_decode_fp8(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(block_tables), _ptr(seq_lens), _ptr(o),
+                                   _ptr(lse), B, Hq, Hkv, q_len, D, nblk, width, bs,
+                                   int(bool(causal)), float(scale), int(num_splits),
+                                   _ptr(workspace), ws_bytes, _stream(q.device, stream))
+    _check(st, "attn_paged_decode_fp8")
+    return (o, lse) if (return_lse or lse is not None) else o
 
 
 class KVCacheAllocator:

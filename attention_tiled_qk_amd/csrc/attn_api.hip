@@ -19,7 +19,8 @@ hipError_t launch_paged_prefill_bf16(const void*, const void*, const void*, cons
 int paged_prefill_max_blocks();
 hipError_t launch_prefill_f32(const void*, const void*, const void*, void*, float*, int, int, int,
                               int, int, float, hipStream_t);
-hipError_t launch_paged_attn(const void*, const void*, const void*, const int32_t*,
+hipError_t launch_paged_attn(const void*, const void*, const void*, const float*, const float*,
+                             const int32_t*,
                              const int32_t*, void*, float*, float*, float*, int, int, int, int, int,
                              int, int, int, float, hipStream_t);
 hipError_t launch_lse_merge(const float*, const float*, void*, float*, long long, int, int, int,
@@ -30,6 +31,11 @@ hipError_t launch_paged_append(const void*, const void*, void*, void*, const int
                                const int32_t*, int, int, int, int, int, hipStream_t);
 hipError_t launch_paged_copy_blocks(void*, void*, const int32_t*, const int32_t*, int, int, int,
                                     hipStream_t);
+hipError_t launch_paged_append_fp8(const void*, const void*, void*, void*, float*, float*,
+                                   const int32_t*, const int32_t*, int, int, int, int, int,
+                                   hipStream_t);
+hipError_t launch_paged_copy_blocks_fp8(void*, void*, float*, float*, const int32_t*,
+                                        const int32_t*, int, int, int, hipStream_t);
 }  // namespace attn
 
 namespace {
@@ -140,7 +146,10 @@ size_t paged_workspace(int B, int Hq, int Hkv, int q_len, int D, int max_blocks_
   return workspace_for(B, Hq, q_len, D, splits_for(B, Hkv, max_blocks_per_seq, num_splits));
 }
 
-int paged_decode(const void* q, const void* k_pool, const void* v_pool,
+// k_scale == nullptr: bf16 pools; otherwise E4M3 pools (one byte per value)
+// with per-(block, head) scales.
+int paged_decode(const void* q, const void* k_pool, const void* v_pool, const float* k_scale,
+                 const float* v_scale,
                  const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse, int B,
                  int Hq, int Hkv, int q_len, int D, int num_blocks, int max_blocks_per_seq,
                  int block_size, int causal, float scale, int num_splits, void* workspace,
@@ -158,13 +167,15 @@ int paged_decode(const void* q, const void* k_pool, const void* v_pool,
   if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
   if (Hkv > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
-  if (checked_mul({num_blocks, Hkv, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
-      checked_mul({B, Hq, q_len, D, 2}) < 0 || (long long)max_blocks_per_seq * 16 > 0x7fffffffLL)
+  if (checked_mul({num_blocks, Hkv, 16, D, k_scale ? 1 : 2}) < 0 ||
+      checked_mul({B, max_blocks_per_seq}) < 0 || checked_mul({B, Hq, q_len, D, 2}) < 0 ||
+      (long long)max_blocks_per_seq * 16 > 0x7fffffffLL)
     return ATTN_ERR_OVERFLOW;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
     return ATTN_ERR_MISALIGNED;
   if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
     return ATTN_ERR_MISALIGNED;
+  if (k_scale && (!aligned4(k_scale) || !aligned4(v_scale))) return ATTN_ERR_MISALIGNED;
   const int S = splits_for(B, Hkv, max_blocks_per_seq, num_splits);
   const size_t need = workspace_for(B, Hq, q_len, D, S);
   float* o_part = nullptr;
@@ -176,7 +187,8 @@ int paged_decode(const void* q, const void* k_pool, const void* v_pool,
     lse_part = o_part + (size_t)B * Hq * q_len * S * D;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = attn::launch_paged_attn(q, k_pool, v_pool, block_tables, seq_lens, o, lse, o_part,
+  hipError_t e = attn::launch_paged_attn(q, k_pool, v_pool, k_scale, v_scale, block_tables,
+                                         seq_lens, o, lse, o_part,
                                          lse_part, B, Hkv, group, q_len, D, max_blocks_per_seq, S,
                                          causal, scale, s);
   if (e != hipSuccess || S == 1) return hip_status(e);
@@ -268,7 +280,8 @@ int attn_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                       int B, int H, int q_len, int D, int num_blocks, int max_blocks_per_seq,
                       int block_size, int causal, float scale, int num_splits, void* workspace,
                       size_t workspace_bytes, int dtype, void* stream) {
-  return paged_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, B, H, H, q_len, D,
+  return paged_decode(q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, o, lse, B, H,
+                      H, q_len, D,
                       num_blocks, max_blocks_per_seq, block_size, causal, scale, num_splits,
                       workspace, workspace_bytes, dtype, stream);
 }
@@ -279,7 +292,8 @@ int attn_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                           int max_blocks_per_seq, int block_size, int causal, float scale,
                           int num_splits, void* workspace, size_t workspace_bytes, int dtype,
                           void* stream) {
-  return paged_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, B, Hq, Hkv, q_len, D,
+  return paged_decode(q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, o, lse, B, Hq,
+                      Hkv, q_len, D,
                       num_blocks, max_blocks_per_seq, block_size, causal, scale, num_splits,
                       workspace, workspace_bytes, dtype, stream);
 }
@@ -355,6 +369,60 @@ int attn_paged_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const
   if (!aligned4(src) || !aligned4(dst)) return ATTN_ERR_MISALIGNED;
   return hip_status(attn::launch_paged_copy_blocks(k_pool, v_pool, src, dst, n, H, D,
                                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                          const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                          int q_len, int D, int num_blocks, int max_blocks_per_seq,
+                          int block_size, int causal, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_scale || !v_scale) return ATTN_ERR_NULL_PTR;
+  return paged_decode(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, o, lse, B, Hq,
+                      Hkv, q_len, D, num_blocks, max_blocks_per_seq, block_size, causal, scale,
+                      num_splits, workspace, workspace_bytes, ATTN_BF16, stream);
+}
+
+int attn_paged_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                          float* k_scale, float* v_scale, const int32_t* block_tables,
+                          const int32_t* seq_lens, int B, int H, int n_new, int D,
+                          int num_blocks, int max_blocks_per_seq, int block_size, void* stream) {
+  if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables ||
+      !seq_lens)
+    return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || H <= 0 || n_new <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != ATTN_BLOCK_SIZE) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)n_new > (long long)max_blocks_per_seq * 16) return ATTN_ERR_BAD_SHAPE;
+  if (H > 65535 || B > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({B, H, n_new, D, 2}) < 0 || checked_mul({num_blocks, H, 16, D}) < 0 ||
+      checked_mul({B, max_blocks_per_seq}) < 0)
+    return ATTN_ERR_OVERFLOW;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return ATTN_ERR_MISALIGNED;
+  if (!aligned4(k_scale) || !aligned4(v_scale) || !aligned4(block_tables) || !aligned4(seq_lens))
+    return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_paged_append_fp8(k_new, v_new, k_pool, v_pool, k_scale, v_scale,
+                                                  block_tables, seq_lens, B, H, n_new, D,
+                                                  max_blocks_per_seq,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                               const int32_t* src, const int32_t* dst, int n, int num_blocks,
+                               int H, int D, void* stream) {
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !src || !dst) return ATTN_ERR_NULL_PTR;
+  if (n <= 0 || num_blocks <= 0 || H <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (n > 65535) return ATTN_ERR_OVERFLOW;
+  if (checked_mul({num_blocks, H, 16, D}) < 0) return ATTN_ERR_OVERFLOW;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_MISALIGNED;
+  if (!aligned4(k_scale) || !aligned4(v_scale) || !aligned4(src) || !aligned4(dst))
+    return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_paged_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src, dst,
+                                                       n, H, D,
+                                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -24,6 +24,16 @@
 //     per-wave LDS area and read back with ds_read_b64_tr_b16;
 //   * block ids are wave-uniform scalar loads; slots past the split's end are
 //     masked in S and zeroed in V (a NaN there must not reach O).
+//
+// FP8 cache (F8): each (block, head) slab holds 16 x D E4M3 codes and one
+// float32 scale per pool (the block-wise quantisation of the FlashAttention-3
+// item of [P3]; [P2] §五 deploys an FP8 KV cache). A lane loads D/4 contiguous
+// code bytes of its K row; the contraction order inside the MFMA is free, so Q
+// is loaded in the matching permuted order. Codes become bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1); the K scale multiplies the block's
+// scores and the V scale its P, so the cache is read at one byte per value.
+#include <type_traits>
+
 #include "common.h"
 
 namespace attn {
@@ -33,9 +43,18 @@ constexpr int kIdChunk = 256;  // block ids staged in LDS at a time (even)
 // WPS waves per workgroup share one (split, head, sequence): wave w takes the
 // w-th part of the split's blocks and the parts are merged in LDS at the end,
 // which gives short-split launches more waves without more partials.
-template <int D, int WPS>
+// Two E4M3 codes (the low or high half of a word) to two bf16, exactly.
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+template <int D, int WPS, bool F8>
 __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k_pool, const bf16* __restrict__ v_pool,
+    const bf16* __restrict__ q, const void* __restrict__ k_pool_, const void* __restrict__ v_pool_,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o_part,
     float* __restrict__ lse_part, int H, int group, int q_len, int max_blocks, int num_splits,
@@ -45,6 +64,12 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   constexpr int PV = D * 2 + 64;        // LDS row pitch of a V slab (bytes)
   constexpr int VCH = 16 * D / 8 / 64;  // 16-byte pieces of one slab per lane
   constexpr int CPR = D / 8;            // 16-byte pieces per slab row
+  constexpr int KR = D / 64;            // fp8: 16-byte K pieces per lane (D/4 codes of a row)
+  constexpr int VR = D / 64;            // fp8: 16-byte V pieces per lane
+  constexpr int CPR8 = D / 16;          // fp8: 16-byte pieces per slab row
+  using KV = std::conditional_t<F8, uint8_t, bf16>;
+  const KV* k_pool = static_cast<const KV*>(k_pool_);
+  const KV* v_pool = static_cast<const KV*>(v_pool_);
   __shared__ __attribute__((aligned(16))) unsigned char vlds_raw[WPS][2 * 16 * PV];
   __shared__ int ids_raw[WPS][kIdChunk];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -100,11 +125,13 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   bf16x8 qreg[DC];
   {
     const bool ok = l16 < ncols;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + qrow * D + 8 * g);
     const unsigned flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      u32x4 w = ok ? src[c * 4] : u32x4{0, 0, 0, 0};
+      // contraction slot (c, g, 0..7) holds d = 32c + 8g + i, or for FP8 the
+      // lane-contiguous order d = g D/4 + 8c + i that the K loads use
+      const int d0 = F8 ? g * (D / 4) + 8 * c : 32 * c + 8 * g;
+      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(q + qrow * D + d0) : u32x4{0, 0, 0, 0};
       w ^= flip;
       qreg[c] = __builtin_bit_cast(bf16x8, w);
     }
@@ -126,10 +153,16 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
 
   // K operands (row l16 of each slab) and V pieces (contiguous per instruction)
   // of the block pair n, n+1. A missing second block reads as zeros.
-  struct Pair {
+  struct PairB {
     bf16x8 ka[DC], kb[DC];
     u32x4 va[VCH], vb[VCH];
   };
+  // FP8: raw code bytes and the two blocks' scales
+  struct PairF {
+    u32x4 ka[KR], kb[KR], va[VR], vb[VR];
+    float ska, skb, sva, svb;
+  };
+  using Pair = std::conditional_t<F8, PairF, PairB>;
   // the block ids of the current chunk [c0, c1) of this split sit in LDS;
   // an id is read with a wave-uniform LDS load (no wait on global loads)
   int c0 = blk0, c1 = blk0;
@@ -137,6 +170,36 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   auto load = [&](int n, Pair& r) {
     const bool has_b = n + 1 < c1;
     const int pa = block_id(n);
+    if constexpr (F8) {
+      const uint8_t* ka_src = k_pool + (size_t)pa * blk_stride + head_off;
+      const uint8_t* va_src = v_pool + (size_t)pa * blk_stride + head_off;
+#pragma unroll
+      for (int i = 0; i < KR; ++i)
+        r.ka[i] = *reinterpret_cast<const u32x4*>(ka_src + l16 * D + g * (D / 4) + 16 * i);
+#pragma unroll
+      for (int i = 0; i < VR; ++i) r.va[i] = *reinterpret_cast<const u32x4*>(va_src + (i * 64 + lane) * 16);
+      r.ska = k_scale[(size_t)pa * H + h];
+      r.sva = v_scale[(size_t)pa * H + h];
+      if (has_b) {
+        const int pb = block_id(n + 1);
+        const uint8_t* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
+        const uint8_t* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
+#pragma unroll
+        for (int i = 0; i < KR; ++i)
+          r.kb[i] = *reinterpret_cast<const u32x4*>(kb_src + l16 * D + g * (D / 4) + 16 * i);
+#pragma unroll
+        for (int i = 0; i < VR; ++i) r.vb[i] = *reinterpret_cast<const u32x4*>(vb_src + (i * 64 + lane) * 16);
+        r.skb = k_scale[(size_t)pb * H + h];
+        r.svb = v_scale[(size_t)pb * H + h];
+      } else {
+#pragma unroll
+        for (int i = 0; i < KR; ++i) r.kb[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < VR; ++i) r.vb[i] = u32x4{0, 0, 0, 0};
+        r.skb = 0.f;
+        r.svb = 0.f;
+      }
+    } else {
     const bf16* ka_src = k_pool + (size_t)pa * blk_stride + head_off;
     const bf16* va_src = v_pool + (size_t)pa * blk_stride + head_off;
 #pragma unroll
@@ -159,26 +222,57 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
 #pragma unroll
       for (int i = 0; i < VCH; ++i) r.vb[i] = u32x4{0, 0, 0, 0};
     }
+    }
   };
 
   auto compute = [&](int n, Pair& r) {
     const int key0 = n * 16;
     const bool tail = key0 + 32 > key_end;
     if (tail) {  // V rows at or past the split's end must be exactly zero
+      if constexpr (F8) {
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) {
-        const int row = (i * 64 + lane) / CPR;
-        if (key0 + row >= key_end) r.va[i] = u32x4{0, 0, 0, 0};
-        if (key0 + 16 + row >= key_end) r.vb[i] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < VR; ++i) {
+          const int row = (i * 64 + lane) / CPR8;
+          if (key0 + row >= key_end) r.va[i] = u32x4{0, 0, 0, 0};
+          if (key0 + 16 + row >= key_end) r.vb[i] = u32x4{0, 0, 0, 0};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int row = (i * 64 + lane) / CPR;
+          if (key0 + row >= key_end) r.va[i] = u32x4{0, 0, 0, 0};
+          if (key0 + 16 + row >= key_end) r.vb[i] = u32x4{0, 0, 0, 0};
+        }
       }
     }
 
     // S^T[key][query] for both blocks
     f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (F8) {
+      // chunk c is bytes 8c .. 8c+7 of the lane's D/4 codes: two words
+      auto kop = [](const u32x4* raw, int c) -> bf16x8 {
+        const uint32_t w0 = raw[c >> 1][(c & 1) * 2];
+        const uint32_t w1 = raw[c >> 1][(c & 1) * 2 + 1];
+        u32x4 o4;
+        o4[0] = fp8x2_lo(w0);
+        o4[1] = fp8x2_hi(w0);
+        o4[2] = fp8x2_lo(w1);
+        o4[3] = fp8x2_hi(w1);
+        return __builtin_bit_cast(bf16x8, o4);
+      };
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      sa = mfma16(r.ka[c], qreg[c], sa);
-      sb = mfma16(r.kb[c], qreg[c], sb);
+      for (int c = 0; c < DC; ++c) {
+        sa = mfma16(kop(r.ka, c), qreg[c], sa);
+        sb = mfma16(kop(r.kb, c), qreg[c], sb);
+      }
+      sa *= r.ska;
+      sb *= r.skb;
+    } else {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        sa = mfma16(r.ka[c], qreg[c], sa);
+        sb = mfma16(r.kb[c], qreg[c], sb);
+      }
     }
 
     if (tail || (causal && key0 + 31 > qpos0)) {
@@ -212,6 +306,13 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
       e[4 + j] = exp2_fast(__builtin_fmaf(sb[j], cs, -mc));
     }
     l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    if constexpr (F8) {  // the V scales of the two blocks go into P
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] *= r.sva;
+        e[4 + j] *= r.svb;
+      }
+    }
     u32x4 pw;
     pw[0] = pack_bf16x2(e[0], e[1]);
     pw[1] = pack_bf16x2(e[2], e[3]);
@@ -222,13 +323,39 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
     // V slabs -> LDS (row-major, padded rows), then transposing reads. The
     // workgroup is this one wave, whose LDS accesses execute in program order,
     // so no barrier is needed (and none may wait for the next pair's loads).
+    if constexpr (F8) {  // 16 codes per piece -> 16 bf16 (two 16-byte LDS stores)
+      auto widen = [](const u32x4& w, u32x4& lo, u32x4& hi) {
+        lo[0] = fp8x2_lo(w[0]);
+        lo[1] = fp8x2_hi(w[0]);
+        lo[2] = fp8x2_lo(w[1]);
+        lo[3] = fp8x2_hi(w[1]);
+        hi[0] = fp8x2_lo(w[2]);
+        hi[1] = fp8x2_hi(w[2]);
+        hi[2] = fp8x2_lo(w[3]);
+        hi[3] = fp8x2_hi(w[3]);
+      };
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int piece = i * 64 + lane;
-      const int row = piece / CPR;
-      const int col = piece % CPR;
-      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 16) = r.va[i];
-      *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 16) = r.vb[i];
+      for (int i = 0; i < VR; ++i) {
+        const int piece = i * 64 + lane;
+        const int row = piece / CPR8;
+        const int col = piece % CPR8;
+        u32x4 lo, hi;
+        widen(r.va[i], lo, hi);
+        *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 32) = lo;
+        *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 32 + 16) = hi;
+        widen(r.vb[i], lo, hi);
+        *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 32) = lo;
+        *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 32 + 16) = hi;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int piece = i * 64 + lane;
+        const int row = piece / CPR;
+        const int col = piece % CPR;
+        *reinterpret_cast<ATTN_LDS u32x4*>(vlds + row * PV + col * 16) = r.va[i];
+        *reinterpret_cast<ATTN_LDS u32x4*>(vlds + (16 + row) * PV + col * 16) = r.vb[i];
+      }
     }
     const ATTN_LDS unsigned char* rd = vlds + (4 * g + (l16 >> 2)) * PV + 8 * (l16 & 3);
 #pragma unroll
@@ -392,18 +519,46 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(const bf16* __restric
   *reinterpret_cast<u32x4*>(out + dst) = *reinterpret_cast<const u32x4*>(pool + src);
 }
 
-template <int D, int WPS>
-static void launch_paged_variant(dim3 grid, hipStream_t stream, const void* q, const void* k_pool,
-                                 const void* v_pool, const int32_t* block_tables,
-                                 const int32_t* seq_lens, void* o, float* lse, float* o_part,
-                                 float* lse_part, int H, int group, int q_len, int max_blocks,
-                                 int num_splits, int causal, float scale) {
-  hipLaunchKernelGGL((paged_attn_kernel<D, WPS>), grid, dim3(64 * WPS), 0, stream, (const bf16*)q,
-                     (const bf16*)k_pool, (const bf16*)v_pool, block_tables, seq_lens, (bf16*)o,
-                     lse, o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
+struct PagedArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  float* o_part;
+  float* lse_part;
+  int H, group, q_len, max_blocks, num_splits, causal;
+  float scale;
+};
+
+template <int D, int WPS, bool F8>
+static void launch_paged_variant(dim3 grid, hipStream_t stream, const PagedArgs& a) {
+  hipLaunchKernelGGL((paged_attn_kernel<D, WPS, F8>), grid, dim3(64 * WPS), 0, stream,
+                     (const bf16*)a.q, a.k_pool, a.v_pool, a.k_scale, a.v_scale, a.block_tables,
+                     a.seq_lens, (bf16*)a.o, a.lse, a.o_part, a.lse_part, a.H, a.group, a.q_len,
+                     a.max_blocks, a.num_splits, a.causal, a.scale);
 }
 
+template <bool F8>
+static void launch_paged_dispatch(int D, bool two, dim3 grid, hipStream_t stream,
+                                  const PagedArgs& a) {
+  if (D == 128) {
+    if (two) launch_paged_variant<128, 2, F8>(grid, stream, a);
+    else launch_paged_variant<128, 1, F8>(grid, stream, a);
+  } else {
+    if (two) launch_paged_variant<64, 2, F8>(grid, stream, a);
+    else launch_paged_variant<64, 1, F8>(grid, stream, a);
+  }
+}
+
+// k_scale == nullptr: bf16 pools; otherwise E4M3 pools with per-(block, head)
+// float32 scales.
 hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_pool,
+                             const float* k_scale, const float* v_scale,
                              const int32_t* block_tables, const int32_t* seq_lens, void* o,
                              float* lse, float* o_part, float* lse_part, int B, int H, int group,
                              int q_len, int D, int max_blocks, int num_splits, int causal,
@@ -412,21 +567,10 @@ hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_po
   // With few (split, head, sequence) items the resident waves would leave part
   // of the chip idle in the last round; give each item two waves instead.
   const bool two = (long long)num_splits * H * B < 4096;
-  if (D == 128) {
-    if (two)
-      launch_paged_variant<128, 2>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                   o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
-    else
-      launch_paged_variant<128, 1>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                   o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
-  } else {
-    if (two)
-      launch_paged_variant<64, 2>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                  o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
-    else
-      launch_paged_variant<64, 1>(grid, stream, q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-                                  o_part, lse_part, H, group, q_len, max_blocks, num_splits, causal, scale);
-  }
+  const PagedArgs a{q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, o, lse, o_part,
+                    lse_part, H, group, q_len, max_blocks, num_splits, causal, scale};
+  if (k_scale != nullptr) launch_paged_dispatch<true>(D, two, grid, stream, a);
+  else launch_paged_dispatch<false>(D, two, grid, stream, a);
   return hipGetLastError();
 }
 

@@ -21,11 +21,13 @@ The same run also measures, under ``secondary``:
     512-token chunk after a 3584-token cached prefix;
   * append: writing that 512-token chunk's K and V into the paged pools
     (attn_paged_append), priced against HBM bandwidth;
+  * c4f8: the c4 decode over an FP8 (E4M3) cache with per-(block, head)
+    scales (attn_paged_decode_fp8): one byte per cached value;
 each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
-``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, cpf, append, or ``copy``: a plain
+``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, cpf, append, c4f8, or ``copy``: a plain
 device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
 its entry; that is the form the profiler runs use.
 
@@ -295,6 +297,62 @@ def bench_paged_prefill(torch, api, spec, warmup, steps, key):
     }
 
 
+def bench_paged_fp8(torch, api, spec, warmup, steps, key):
+    import ctypes
+    from workloads import paged_inputs_fp8
+    log(f"[bench] building {spec.name} inputs")
+    inp = paged_inputs_fp8(spec)
+    dq, dk, dv, dks, dvs, dt, dl = (t.cuda() for t in (inp.q, inp.k_codes, inp.v_codes,
+                                                        inp.k_scale, inp.v_scale,
+                                                        inp.block_tables, inp.seq_lens))
+    lens = inp.seq_lens.tolist()
+    B, Hq, q_len, D = inp.q.shape
+    H = inp.k_codes.shape[1]
+    width = inp.block_tables.shape[1]
+    ws_bytes = api.attn_paged_gqa_workspace_bytes(B, Hq, H, q_len, D, width, spec.num_splits)
+    ws = torch.empty(max(ws_bytes // 4, 1), device="cuda", dtype=torch.float32)
+    o = torch.empty_like(dq)
+    api.attn_paged_decode_fp8(dq, dk, dv, dks, dvs, dt, dl, causal=spec.causal, scale=spec.scale,
+                              num_splits=spec.num_splits, o=o, workspace=ws)  # validates once
+    P = ctypes.c_void_p
+    args = (P(dq.data_ptr()), P(dk.data_ptr()), P(dv.data_ptr()), P(dks.data_ptr()),
+            P(dvs.data_ptr()), P(dt.data_ptr()), P(dl.data_ptr()), P(o.data_ptr()), None, B, Hq,
+            H, q_len, D, dk.shape[0], width, 16, int(spec.causal), ctypes.c_float(spec.scale),
+            spec.num_splits, P(ws.data_ptr()), ctypes.c_size_t(ws.numel() * 4),
+            P(torch.cuda.current_stream().cuda_stream))
+    fn = api.lib.attn_paged_decode_fp8
+
+    def call():
+        if fn(*args) != 0:
+            raise RuntimeError("attn_paged_decode_fp8 failed")
+
+    ms, wall = time_launches(torch, call, warmup, steps)
+    # one byte per cached K and V value, plus the two scales of each (block, head)
+    blocks = sum(-(-n // 16) for n in lens)
+    kv = 2.0 * H * D * sum(lens) + 2.0 * 4 * H * blocks
+    gbs = kv / (ms * 1e-3) / 1e9
+    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})")
+    del dq, dk, dv, dks, dvs, dt, dl, ws, o
+    torch.cuda.empty_cache()
+    return {
+        "workload": spec.name,
+        "num_splits": spec.num_splits if spec.num_splits else "auto",
+        "ms_per_step": wall / steps,
+        "value": kv / (wall / steps * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "paged_attn_kernel<128, fp8> (+ lse_merge_kernel when split)",
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": load_traffic(key, source_digest(*KERNEL_SOURCES["paged"])),
+            "algorithmic_bytes_per_launch": kv,
+            "launch_us_events": ms * 1e3,
+        },
+    }
+
+
 def bench_append(torch, api, spec, warmup, steps, key):
     """K/V of one q_len-token chunk per sequence written into the pools."""
     import ctypes
@@ -362,7 +420,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "cpf", "append", "copy"],
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8", "copy"],
                     help="run one workload and print its entry only")
     args = ap.parse_args()
 
@@ -378,7 +436,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import attention_tiled_qk_amd as api
-    from workloads import C2, C3, C4, C4G, C5, CPF
+    from workloads import C2, C3, C4, C4F8, C4G, C5, CPF
 
     steps, warmup = args.steps, args.warmup
     runners = {
@@ -389,6 +447,7 @@ def main():
         "c4g": lambda: bench_paged(torch, api, C4G, warmup, max(steps // 2, 3), "paged_c4g"),
         "cpf": lambda: bench_paged_prefill(torch, api, CPF, warmup, max(steps // 2, 3), "prefill_cpf"),
         "append": lambda: bench_append(torch, api, CPF, warmup, max(steps // 2, 3), "append_cpf"),
+        "c4f8": lambda: bench_paged_fp8(torch, api, C4F8, warmup, max(steps // 2, 3), "paged_c4f8"),
         "copy": lambda: bench_copy(torch, warmup, steps),
     }
     if args.only:
@@ -413,7 +472,7 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
-        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g", "cpf", "append")},
+        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g", "cpf", "append", "c4f8")},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")

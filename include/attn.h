@@ -371,6 +371,71 @@ int attn_kv_cache_block_refs(const attn_kv_cache* cache, int block);
  * device for the attention and append calls. */
 int attn_kv_cache_export(const attn_kv_cache* cache, int32_t* block_tables, int32_t* seq_lens);
 
+/*
+ * FP8 KV cache with block-wise scales. The FlashAttention-3 item of [P3] lists
+ * FP8 (E4M3 / E5M2) data for the attention products with block-wise
+ * quantisation -- each block carries its own scale factor -- and [P2] §五
+ * deploys an FP8 KV cache. Here each (physical block, head) of the K pool and
+ * of the V pool holds 16 x D E4M3 codes (OCP format: bias 7, max 448, codes
+ * 0x7F / 0xFF NaN) and one float32 scale; the stored value is
+ * decode(code) * scale. Pools are uint8 [num_blocks, H, 16, D]; scales are
+ * float32 [num_blocks, H]. The cache is read at one byte per value, half the
+ * bytes of a bf16 cache.
+ */
+
+/*
+ * attn_paged_append_fp8 -- write n_new new bf16 tokens of K and V into FP8
+ * pools (positions as for attn_paged_append). For each (block, head) that
+ * receives tokens: s_old is its stored scale, or 0 when the append starts at
+ * slot 0 of the block (a fresh block: a stale scale is ignored);
+ * s_new = max(s_old, max|new values| / 448); if s_new > s_old the block's
+ * earlier slots are re-encoded as e4m3((decode(code) * s_old) / s_new); new
+ * values are stored as e4m3(x / s_new) (0 when s_new = 0). Float32 arithmetic,
+ * IEEE division, round to nearest even after clamping to +-448. New values
+ * must be finite.
+ *
+ *   k_new, v_new     : [B, H, n_new, D] bf16.
+ *   k_pool, v_pool   : [num_blocks, H, 16, D] uint8 (E4M3 codes), in place.
+ *   k_scale, v_scale : [num_blocks, H] float32, in place.
+ *   block_tables, seq_lens, D, block_size: as for attn_paged_append.
+ * Sequences must not share a destination block. Returns ATTN_OK or a negative
+ * ATTN_ERR_* code.
+ */
+int attn_paged_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                          float* k_scale, float* v_scale, const int32_t* block_tables,
+                          const int32_t* seq_lens, int B, int H, int n_new, int D,
+                          int num_blocks, int max_blocks_per_seq, int block_size, void* stream);
+
+/*
+ * attn_paged_copy_blocks_fp8 -- attn_paged_copy_blocks for FP8 pools: copies
+ * the codes of block src[i] onto dst[i] in both pools, and its H scales in both
+ * scale arrays. Bit-exact.
+ */
+int attn_paged_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                               const int32_t* src, const int32_t* dst, int n, int num_blocks,
+                               int H, int D, void* stream);
+
+/*
+ * attn_paged_decode_fp8 -- attn_paged_decode_gqa over FP8 pools: the keys and
+ * values are decode(code) * scale of their (block, head). q and o stay bf16;
+ * codes are widened to bf16 exactly on chip, the K scale multiplies the
+ * block's scores and the V scale its probabilities (float32 accumulation).
+ *
+ *   q, o             : [B, Hq, q_len, D] bf16.
+ *   k_pool, v_pool   : [num_blocks, Hkv, 16, D] uint8 E4M3 codes.
+ *   k_scale, v_scale : [num_blocks, Hkv] float32.
+ *   workspace        : at least attn_paged_gqa_workspace_bytes(B, Hq, Hkv,
+ *                      q_len, D, max_blocks_per_seq, num_splits) bytes.
+ *   Every other argument as for attn_paged_decode_gqa (Hq == Hkv is plain
+ *   multi-head attention). Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                          const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                          int q_len, int D, int num_blocks, int max_blocks_per_seq,
+                          int block_size, int causal, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_string(int status);
 

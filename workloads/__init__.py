@@ -15,6 +15,11 @@ the CPU, in the order listed, so the same seed gives the same bytes anywhere):
   in every row); unused table entries are -1. Pools are [num_blocks, H, 16, D].
   Tail slots past seq_len hold random values too (or NaN when ``poison``), and
   ``extra_blocks`` adds pool blocks that no table references.
+* FP8 paged (E4M3 codes with per-(block, head) float32 scales): the same
+  layout draws, then K codes, V codes, K scales, V scales, q. A code is a
+  uniform sign bit over a uniform magnitude code in [0x30, 0x70] (values
+  0.5 .. 128 before scaling); scales are uniform in [1e-3, 4e-3]. With
+  ``poison`` every slot no sequence may read holds the NaN code 0x7F.
 """
 
 import math
@@ -88,7 +93,12 @@ C4G = PagedSpec("gqa_paged_decode_bf16_64seq_64qh_8kvh_len128-4096", 64, 8, 1, 1
 # sequences x 40 heads, a 512-token chunk after a 3584-token cached prefix.
 CPF = PagedSpec("chunked_prefill_bf16_8seq_40h_chunk512_len4096", 8, 40, 512, 128, 7,
                 fixed_len=4096)
-CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c4g": C4G, "cpf": CPF}
+# FP8 cache (a follow-on of the paged path): the c4 decode workload with E4M3
+# K/V codes and per-(block, head) scales.
+C4F8 = PagedSpec("fp8_paged_decode_64seq_40h_len128-4096", 64, 40, 1, 128, 8,
+                 len_lo=128, len_hi=4096)
+CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c4g": C4G, "cpf": CPF,
+           "c4f8": C4F8}
 
 
 def _randn(gen, shape, dtype):
@@ -151,6 +161,44 @@ def paged_inputs(spec):
     if spec.poison:
         _poison(k_pool, v_pool, lens, tables)
     return PagedInputs(q, k_pool, v_pool, tables, lens, perm)
+
+
+@dataclass
+class PagedInputsFp8:
+    q: torch.Tensor            # [B, Hq, q_len, D] bf16
+    k_codes: torch.Tensor      # [num_blocks, H, 16, D] uint8 E4M3 codes
+    v_codes: torch.Tensor
+    k_scale: torch.Tensor      # [num_blocks, H] float32
+    v_scale: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+
+
+def paged_inputs_fp8(spec):
+    """FP8 paged inputs on the CPU for a PagedSpec (recipe in the module docstring)."""
+    g = torch.Generator().manual_seed(spec.seed)
+    lens, tables, total, _ = paged_layout(spec, g)
+    shape = (total, spec.H, BLOCK, spec.D)
+
+    def codes():
+        mag = torch.randint(0x30, 0x71, shape, generator=g, dtype=torch.uint8)
+        sign = torch.randint(0, 2, shape, generator=g, dtype=torch.uint8) * 0x80
+        return mag | sign
+
+    k, v = codes(), codes()
+    ks = torch.rand((total, spec.H), generator=g) * 3e-3 + 1e-3
+    vs = torch.rand((total, spec.H), generator=g) * 3e-3 + 1e-3
+    q = _randn(g, (spec.B, spec.q_heads or spec.H, spec.q_len, spec.D), "bf16")
+    if spec.poison:
+        readable = torch.zeros(total, BLOCK, dtype=torch.bool)
+        for b in range(tables.shape[0]):
+            n = int(lens[b])
+            for t0 in range(0, n, BLOCK):
+                readable[int(tables[b, t0 // BLOCK]), : min(BLOCK, n - t0)] = True
+        idx = (~readable).nonzero(as_tuple=True)
+        k[idx[0], :, idx[1], :] = 0x7F
+        v[idx[0], :, idx[1], :] = 0x7F
+    return PagedInputsFp8(q, k, v, ks, vs, tables, lens)
 
 
 def _poison(k_pool, v_pool, lens, tables):
