@@ -33,7 +33,9 @@
 //     moved, l and O rescaled and P recomputed -- rare after the first tile;
 //   * causal: key tiles above a wave's last row are skipped, the mask is only
 //     evaluated on tiles that cross the diagonal, and the work order (tile_of)
-//     keeps each head on one XCD and starts the longest query tiles first.
+//     keeps each head on one XCD and starts the longest query tiles first;
+//     launches with evenly loaded tiles (full attention, paged chunks) run a
+//     head's query tiles side by side instead (tile_of_head_major).
 #include <type_traits>
 
 #include "common.h"
@@ -91,6 +93,23 @@ __device__ __forceinline__ void tile_of(int id, int n_heads, int n_qtiles, int& 
   }
 }
 
+// Head-major work order, for launches whose query tiles carry similar work
+// (full attention; a chunk after a long cached prefix): the query tiles of one
+// head get consecutive ids on the same XCD, so they run together and stream
+// that head's K/V through its L2 once instead of once per tile.
+__device__ __forceinline__ void tile_of_head_major(int id, int n_heads, int n_qtiles, int& bh,
+                                                   int& qt) {
+  if ((n_heads & 7) == 0) {
+    const int hpx = n_heads >> 3;
+    const int pos = id >> 3;
+    bh = (id & 7) * hpx + pos / n_qtiles;
+    qt = n_qtiles - 1 - pos % n_qtiles;
+  } else {
+    bh = id / n_qtiles;
+    qt = n_qtiles - 1 - id % n_qtiles;
+  }
+}
+
 }  // namespace
 
 // Where the keys come from when the kernel runs over a paged cache: the
@@ -126,7 +145,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int g = lane >> 5;
 
   int bh, qt;
-  tile_of(blockIdx.x, n_heads, n_qtiles, bh, qt);
+  if (CAUSAL && !PAGED) tile_of(blockIdx.x, n_heads, n_qtiles, bh, qt);
+  else tile_of_head_major(blockIdx.x, n_heads, n_qtiles, bh, qt);
   // L queries per head; Lk keys, the last L of which are the queries' own
   // positions (Lk == L for dense prefill). Query row r sits at position off + r.
   const size_t head_off = (size_t)bh * L * D;  // dense K, V of this head
