@@ -530,10 +530,10 @@ def test_gather_paging_figure(api):
 
 # -------------------------------------------------------------------- merge ---
 
-@pytest.mark.parametrize("S", [1, 3, 16])
-def test_lse_merge(api, S):
+@pytest.mark.parametrize("S,D", [(1, 128), (3, 128), (16, 128), (1024, 128), (7, 64)])
+def test_lse_merge(api, S, D):
     g = torch.Generator().manual_seed(S)
-    B, H, ql, D = 2, 3, 5, 128
+    B, H, ql = 2, 3, 5
     op = torch.randn(B, H, ql, S, D, generator=g)
     lp = torch.randn(B, H, ql, S, generator=g) * 3
     if S > 1:
@@ -546,6 +546,36 @@ def test_lse_merge(api, S):
     assert max_err(o32, ref_o) <= TOL_F32
     assert max_err(obf, ref_o) <= TOL_BF16
     assert lse_err(l32, ref_l) <= TOL_F32
+
+
+# ------------------------------------------------------ largest shapes ---
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_prefill_widest_table(api, causal):
+    """A sequence of 32768 keys: the full 2048-entry table the paged prefill
+    kernel stages in LDS, with a ragged 200-token chunk."""
+    inp = _paged((32768,), 200, H=2, seed=95, extra=0, poison=False)
+    assert inp.block_tables.shape[1] >= 2048
+    tables = inp.block_tables[:, :2048].contiguous()
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, tables, inp.seq_lens,
+                                            1 / math.sqrt(128), causal)
+    o, lse = api.attn_paged_prefill(*to_dev(inp.q, inp.k_pool, inp.v_pool, tables, inp.seq_lens),
+                                    causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    e, el = max_err(o, ref_o), lse_err(lse, ref_lse)
+    say(f"  32768 keys, causal={causal}: max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_paged_decode_widest_query_and_most_splits(api):
+    """q_len 16 (the column limit) with the largest explicit split count, 64."""
+    inp = _paged((16, 40, 700, 3000), 16, H=2, seed=96)
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, 1 / math.sqrt(128), True)
+    o, lse = _run_paged(api, inp, 64)
+    e, el = max_err(o, ref_o), lse_err(lse, ref_lse)
+    say(f"  q_len 16, S=64: max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_LSE
 
 
 # ------------------------------------------------------ full-size paged ---
