@@ -39,6 +39,7 @@
 namespace attn {
 
 constexpr int kIdChunk = 256;  // block ids staged in LDS at a time (even)
+constexpr float kMaxPairSum = 1073741824.f;  // 2^30: bound on one lane's P sum per block pair
 
 // WPS waves per workgroup share one (split, head, sequence): wave w takes the
 // w-th part of the split's blocks and the parts are merged in LDS at the end,
@@ -143,6 +144,7 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
   const int32_t* table = block_tables + (size_t)b * max_blocks;
 
   float m_run = -INFINITY;
+  float mc_run = 0.f;  // cs * m_run, 0 while m_run is unset
   float l_run = 0.f;
   f32x4 acc[DB];
 #pragma unroll
@@ -285,27 +287,36 @@ __global__ __launch_bounds__(64 * WPS) void paged_attn_kernel(
       }
     }
 
-    float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
-                     fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-    mt = max_xor16(mt);
-    mt = max_xor32(mt);
-    const float m_new = fmaxf(m_run, mt);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-      // lanes whose max did not move keep alpha = 1 (also avoids -inf - -inf)
+    // P = 2^(cs s - mc) against a reference max m (any m gives the same O and
+    // l ratio). The row max is taken, m moved and l, O rescaled only when m is
+    // still unset or some lane's P sum over the pair reaches 2^30; otherwise no
+    // cross-lane reduction and no rescale run for the pair.
+    float e[8];
+    auto probs = [&](float mc) -> float {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = exp2_fast(__builtin_fmaf(sa[j], cs, -mc));
+        e[4 + j] = exp2_fast(__builtin_fmaf(sb[j], cs, -mc));
+      }
+      return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    };
+    float ls = probs(mc_run);
+    if (__builtin_amdgcn_ballot_w64(!(ls < kMaxPairSum) || m_run == -INFINITY) != 0) {
+      float mt = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                       fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+      mt = max_xor16(mt);
+      mt = max_xor32(mt);
+      const float m_new = fmaxf(m_run, mt);
+      // an unchanged m (also -inf == -inf) keeps alpha = 1; m unset before gives 0
       const float alpha = m_new == m_run ? 1.f : exp2_fast((m_run - m_new) * cs);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       m_run = m_new;
+      mc_run = (m_run == -INFINITY ? 0.f : m_run) * cs;
+      ls = probs(mc_run);
     }
-    const float mc = (m_run == -INFINITY ? 0.f : m_run) * cs;
-    float e[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e[j] = exp2_fast(__builtin_fmaf(sa[j], cs, -mc));
-      e[4 + j] = exp2_fast(__builtin_fmaf(sb[j], cs, -mc));
-    }
-    l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    l_run += ls;
     if constexpr (F8) {  // the V scales of the two blocks go into P
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
