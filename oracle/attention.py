@@ -223,14 +223,19 @@ def paged_attention_varlen(q, cu_q_lens, k_pool, v_pool, block_tables, seq_lens,
     cu_q_lens[b+1]-1, its t-th new token at position seq_lens[b] - q_len_b + t
     (bottom-right causal, as in paged_attention). Each sequence is an ordinary
     paged attention problem of its own ([P1] §3.2 cache, [P1] §2.1 attention);
-    continuous batching only packs them into one call. Returns (o [total_q, H,
-    D], lse [total_q, H]) in float64; with ``seqs`` only those sequences are
-    evaluated (the other rows are NaN).
+    continuous batching only packs them into one call. The pools may hold fewer
+    heads than q (grouped-query: query head h reads KV head h // (H / Hkv)).
+    Returns (o [total_q, H, D], lse [total_q, H]) in float64; with ``seqs`` only
+    those sequences are evaluated (the other rows are NaN).
     """
     cu = _i64(cu_q_lens)
     tables = _i64(block_tables)
     lens = _i64(seq_lens)
     total, H, _ = q.shape
+    hkv = k_pool.shape[1]
+    if H % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = H // hkv
     o = np.full((total, H, v_pool.shape[3]), np.nan)
     lse = np.full((total, H), np.nan)
     for b in (range(len(cu) - 1) if seqs is None else seqs):
@@ -240,7 +245,8 @@ def paged_attention_varlen(q, cu_q_lens, k_pool, v_pool, block_tables, seq_lens,
         kc = paged_gather(k_pool, tables[b:b + 1], lens[b:b + 1], block_size)[0]
         vc = paged_gather(v_pool, tables[b:b + 1], lens[b:b + 1], block_size)[0]
         for h in range(H):
-            o[a:e, h], lse[a:e, h] = dense_attention(q[a:e, h], kc[h], vc[h], scale, causal)
+            o[a:e, h], lse[a:e, h] = dense_attention(q[a:e, h], kc[h // group], vc[h // group],
+                                                     scale, causal)
     return o, lse
 
 

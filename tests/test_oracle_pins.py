@@ -396,6 +396,32 @@ def test_paged_varlen_ragged_against_scalar_loops():
             np.testing.assert_allclose(lse[a:e, h], lb, rtol=0, atol=1e-12)
 
 
+def test_paged_varlen_gqa_equals_repeated_kv_heads():
+    """Ragged grouped-query prefill is the ragged multi-head form on a pool
+    whose every KV head is repeated for the query heads of its group."""
+    inp = _small_paged(q_len=1, lens=(20, 33, 7, 50), H=2, D=8)
+    group = 3
+    qlens = [5, 0, 7, 12]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32)
+    g = torch.Generator().manual_seed(4)
+    q = torch.randn(int(cu[-1]), 2 * group, 8, generator=g).to(torch.bfloat16)
+    o, lse = oracle.paged_attention_varlen(q, cu, inp.k_pool, inp.v_pool, inp.block_tables,
+                                           inp.seq_lens, 0.4, True)
+    kr = inp.k_pool.repeat_interleave(group, dim=1)
+    vr = inp.v_pool.repeat_interleave(group, dim=1)
+    o2, l2 = oracle.paged_attention_varlen(q, cu, kr, vr, inp.block_tables, inp.seq_lens, 0.4,
+                                           True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+    # query head 4 (group 1) of sequence 3 against scalar loops over KV head 1
+    kc = oracle.paged_gather(inp.k_pool, inp.block_tables, inp.seq_lens)
+    vc = oracle.paged_gather(inp.v_pool, inp.block_tables, inp.seq_lens)
+    a, e = int(cu[3]), int(cu[4])
+    ob, lb = brute_attention(q[a:e, 4].double().tolist(), kc[3][1].double().tolist(),
+                             vc[3][1].double().tolist(), 0.4, True)
+    np.testing.assert_allclose(o[a:e, 4], ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[a:e, 4], lb, rtol=0, atol=1e-12)
+
+
 def test_paged_gqa_rejects_uneven_heads():
     inp = _small_paged(H=2, D=8)
     q = torch.zeros(inp.q.shape[0], 3, 1, 8, dtype=torch.bfloat16)
