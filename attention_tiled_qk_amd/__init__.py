@@ -19,7 +19,7 @@ from .build import LIB_PATH
 __all__ = [
     "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
     "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_prefill",
-    "attn_paged_prefill_varlen",
+    "attn_paged_prefill_varlen", "attn_paged_prefill_gqa",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
     "KVCacheAllocator", "attn_paged_append_fp8", "attn_paged_copy_blocks_fp8",
     "attn_paged_decode_fp8", "attn_version", "lib", "LIB_PATH", "ATTN_F32", "ATTN_BF16",
@@ -58,6 +58,9 @@ lib.attn_paged_prefill.restype = _i
 lib.attn_paged_prefill_varlen.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                           _i, _i, _i, _f, _i, _p]
 lib.attn_paged_prefill_varlen.restype = _i
+lib.attn_paged_prefill_gqa.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                       _i, _i, _i, _f, _i, _p]
+lib.attn_paged_prefill_gqa.restype = _i
 lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
@@ -230,6 +233,14 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
     return (o, lse) if (return_lse or lse is not None) else o
 
 
+def attn_paged_decode_gqa(q, k_pool, v_pool, block_tables, seq_lens, **kw):
+    """attn_paged_decode with pools of fewer heads than q (grouped-query):
+    q [B, Hq, q_len, D], pools [num_blocks, Hkv, 16, D] with Hkv dividing Hq."""
+    if k_pool.dim() != 4 or q.dim() != 4 or k_pool.shape[1] >= q.shape[1]:
+        raise ValueError("grouped-query decode needs pools with fewer heads than q")
+    return attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, **kw)
+
+
 def attn_paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True, scale=None,
                        o=None, lse=None, return_lse=False, stream=None):
     """Chunked prefill over a paged cache: q [B, H, q_len, D] (bf16), the
@@ -271,7 +282,9 @@ def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_le
     """Ragged chunked prefill over a paged cache: q [total_q, H, D] (bf16,
     token-major), sequence b owning query tokens cu_q_lens[b] .. cu_q_lens[b+1]-1
     (int32 device, B + 1 entries); ``max_q_len`` is the largest of those counts.
-    Returns o [total_q, H, D] (and lse [total_q, H] float32)."""
+    Returns o [total_q, H, D] (and lse [total_q, H] float32). When the pools hold
+    fewer heads than q (a divisor of them), the call goes to
+    attn_paged_prefill_gqa (grouped-query attention)."""
     _dev(q, "q", torch.bfloat16)
     _dev(k_pool, "k_pool", torch.bfloat16)
     _dev(v_pool, "v_pool", torch.bfloat16)
@@ -282,8 +295,8 @@ def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_le
         raise ValueError("q must be [total_q, H, D] and the pools [num_blocks, H, 16, D]")
     total_q, H, D = q.shape
     nblk, Hp, bs, Dp = k_pool.shape
-    if Hp != H or Dp != D:
-        raise ValueError("pool heads / head_dim must match q")
+    if Dp != D or Hp <= 0 or H % Hp != 0:
+        raise ValueError("pool head_dim must match q and pool heads must divide query heads")
     B = seq_lens.shape[0]
     if block_tables.dim() != 2 or block_tables.shape[0] != B or cu_q_lens.shape != (B + 1,):
         raise ValueError("block_tables must be [B, W], seq_lens [B] and cu_q_lens [B + 1]")
@@ -296,13 +309,24 @@ def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_le
         lse = torch.empty((total_q, H), device=q.device, dtype=torch.float32)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
-    st = lib.attn_paged_prefill_varlen(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-                                       _ptr(seq_lens), _ptr(cu_q_lens), _ptr(o), _ptr(lse), B, H,
-                                       total_q, int(max_q_len), D, nblk, block_tables.shape[1],
-                                       bs, int(bool(causal)), float(scale), ATTN_BF16,
-                                       _stream(q.device, stream))
-    _check(st, "attn_paged_prefill_varlen")
+    head = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens),
+            _ptr(cu_q_lens), _ptr(o), _ptr(lse), B, H)
+    tail = (total_q, int(max_q_len), D, nblk, block_tables.shape[1], bs, int(bool(causal)),
+            float(scale), ATTN_BF16, _stream(q.device, stream))
+    if Hp == H:
+        _check(lib.attn_paged_prefill_varlen(*head, *tail), "attn_paged_prefill_varlen")
+    else:
+        _check(lib.attn_paged_prefill_gqa(*head, Hp, *tail), "attn_paged_prefill_gqa")
     return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_paged_prefill_gqa(q, k_pool, v_pool, block_tables, seq_lens, cu_q_lens, max_q_len, **kw):
+    """attn_paged_prefill_varlen with pools of fewer heads than q (grouped-query):
+    q [total_q, Hq, D], pools [num_blocks, Hkv, 16, D] with Hkv dividing Hq."""
+    if k_pool.dim() != 4 or q.dim() != 3 or k_pool.shape[1] >= q.shape[1]:
+        raise ValueError("grouped-query prefill needs pools with fewer heads than q")
+    return attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_lens,
+                                     max_q_len, **kw)
 
 
 def attn_lse_merge(o_part, lse_part, *, out_dtype=torch.bfloat16, o=None, lse=None,

@@ -15,7 +15,7 @@ hipError_t launch_prefill_bf16(const void*, const void*, const void*, void*, flo
                                int, int, float, hipStream_t);
 hipError_t launch_paged_prefill_bf16(const void*, const void*, const void*, const int32_t*,
                                      const int32_t*, void*, float*, int, int, int, int, int, int,
-                                     float, hipStream_t, const int32_t*);
+                                     float, hipStream_t, const int32_t*, int);
 int paged_prefill_max_blocks();
 hipError_t launch_prefill_f32(const void*, const void*, const void*, void*, float*, int, int, int,
                               int, int, float, hipStream_t);
@@ -231,7 +231,8 @@ int attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
   return hip_status(attn::launch_paged_prefill_bf16(q, k_pool, v_pool, block_tables, seq_lens, o,
                                                     lse, B, H, q_len, D, max_blocks_per_seq,
                                                     causal, scale,
-                                                    reinterpret_cast<hipStream_t>(stream), nullptr));
+                                                    reinterpret_cast<hipStream_t>(stream), nullptr,
+                                                    H));
 }
 
 int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_pool,
@@ -240,11 +241,23 @@ int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_p
                               int total_q, int max_q_len, int D, int num_blocks,
                               int max_blocks_per_seq, int block_size, int causal, float scale,
                               int dtype, void* stream) {
+  return attn_paged_prefill_gqa(q, k_pool, v_pool, block_tables, seq_lens, cu_q_lens, o, lse, B,
+                                H, H, total_q, max_q_len, D, num_blocks, max_blocks_per_seq,
+                                block_size, causal, scale, dtype, stream);
+}
+
+int attn_paged_prefill_gqa(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* cu_q_lens, void* o, float* lse, int B, int H, int Hkv,
+                           int total_q, int max_q_len, int D, int num_blocks,
+                           int max_blocks_per_seq, int block_size, int causal, float scale,
+                           int dtype, void* stream) {
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !cu_q_lens || !o)
     return ATTN_ERR_NULL_PTR;
-  if (B <= 0 || H <= 0 || total_q <= 0 || max_q_len <= 0 || num_blocks <= 0 ||
+  if (B <= 0 || H <= 0 || Hkv <= 0 || total_q <= 0 || max_q_len <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0)
     return ATTN_ERR_BAD_SHAPE;
+  if (H % Hkv != 0) return ATTN_ERR_BAD_SHAPE;
   if (max_q_len > total_q) return ATTN_ERR_BAD_SHAPE;
   if (dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
@@ -253,7 +266,7 @@ int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_p
   if ((long long)max_q_len > (long long)max_blocks_per_seq * 16) return ATTN_ERR_BAD_SHAPE;
   if (causal != 0 && causal != 1) return ATTN_ERR_BAD_SHAPE;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
-  if (checked_mul({num_blocks, H, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
+  if (checked_mul({num_blocks, Hkv, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
       checked_mul({total_q, H, D, 4}) < 0)
     return ATTN_ERR_OVERFLOW;
   if ((long long)B * H * ((max_q_len + kPrefillRowsBf16 - 1) / kPrefillRowsBf16) > kMaxGrid)
@@ -267,7 +280,7 @@ int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_p
                                                     lse, B, H, max_q_len, D, max_blocks_per_seq,
                                                     causal, scale,
                                                     reinterpret_cast<hipStream_t>(stream),
-                                                    cu_q_lens));
+                                                    cu_q_lens, Hkv));
 }
 
 size_t attn_paged_gqa_workspace_bytes(int B, int Hq, int Hkv, int q_len, int D,

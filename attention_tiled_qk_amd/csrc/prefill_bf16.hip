@@ -122,8 +122,9 @@ struct PagedKV {
   const int32_t* block_tables;  // [B, max_blocks]
   const int32_t* seq_lens;      // [B], keys per sequence including its new tokens
   const int32_t* cu_q;          // [B + 1] packed query offsets, or null (q_len = L for all)
-  int heads;                    // heads per sequence (pool and queries)
+  int heads;                    // query heads per sequence
   int max_blocks;
+  int kv_heads;                 // heads of the pools; query head h reads h / (heads / kv_heads)
 };
 
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
@@ -156,10 +157,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   size_t row_stride = D;          // elements between consecutive query rows
   size_t lse_off = (size_t)bh * L;
   size_t lse_stride = 1;
-  int Lk = L, hh = 0, seq = 0;
+  int Lk = L, hh = 0, kvh = 0, seq = 0;
   if constexpr (PAGED) {
     seq = bh / pg.heads;
     hh = bh - seq * pg.heads;
+    kvh = hh / (pg.heads / pg.kv_heads);
     Lk = pg.seq_lens[seq];
     if (pg.cu_q != nullptr) {
       const int c0 = pg.cu_q[seq];
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int key = kt * BN + (wave + NW * i) * C::RPP;
     if (key >= Lk) return buffer_rsrc(pool, 0);
     const int blk = __builtin_amdgcn_readfirstlane(ids[key >> 4]);
-    const bf16* src = pool + (((size_t)blk * pg.heads + hh) * 16 + (key & 15)) * D;
+    const bf16* src = pool + (((size_t)blk * pg.kv_heads + kvh) * 16 + (key & 15)) * D;
     return buffer_rsrc(src, min(C::RPP, Lk - key) * C::ROWB);
   };
   auto issue_k = [&](auto s, int kt) {
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
 hipError_t launch_prefill_pipe(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int L, float scale, hipStream_t stream,
-                               PagedKV pg = PagedKV{nullptr, nullptr, nullptr, 0, 0}) {
+                               PagedKV pg = PagedKV{nullptr, nullptr, nullptr, 0, 0, 0}) {
   using C = PrefillCfg<D, NW, BN>;
   const int n_qtiles = (L + C::BM - 1) / C::BM;
   const long long grid = (long long)B * H * n_qtiles;
@@ -484,9 +486,10 @@ hipError_t launch_paged_prefill_bf16(const void* q, const void* k_pool, const vo
                                      const int32_t* block_tables, const int32_t* seq_lens, void* o,
                                      float* lse, int B, int H, int q_len, int D, int max_blocks,
                                      int causal, float scale, hipStream_t stream,
-                                     const int32_t* cu_q) {
-  // with cu_q, q_len is the longest sequence's query count (it sizes the grid)
-  const PagedKV pg{block_tables, seq_lens, cu_q, H, max_blocks};
+                                     const int32_t* cu_q, int Hkv) {
+  // with cu_q, q_len is the longest sequence's query count (it sizes the grid);
+  // H query heads read the pools' Hkv heads in groups of H / Hkv
+  const PagedKV pg{block_tables, seq_lens, cu_q, H, max_blocks, Hkv};
   if (D == 128) {
     return causal ? launch_prefill_pipe<128, 4, 64, true, true>(q, k_pool, v_pool, o, lse, B, H,
                                                                 q_len, scale, stream, pg)

@@ -202,6 +202,22 @@ int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_p
                               int dtype, void* stream);
 
 /*
+ * attn_paged_prefill_gqa -- attn_paged_prefill_varlen over pools with fewer
+ * heads than the queries (grouped-query attention, [P3] TTFT item): H query
+ * heads read Hkv KV heads, query head h reading KV head h / (H / Hkv)
+ * (consecutive query heads form a group). Layouts and every other argument as
+ * for attn_paged_prefill_varlen, except k_pool, v_pool: [num_blocks, Hkv, 16, D]
+ * bf16. H must be a multiple of Hkv (else ATTN_ERR_BAD_SHAPE); with H == Hkv it
+ * is attn_paged_prefill_varlen.
+ */
+int attn_paged_prefill_gqa(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* cu_q_lens, void* o, float* lse, int B, int H, int Hkv,
+                           int total_q, int max_q_len, int D, int num_blocks,
+                           int max_blocks_per_seq, int block_size, int causal, float scale,
+                           int dtype, void* stream);
+
+/*
  * attn_paged_decode_gqa -- attn_paged_decode with grouped-query attention:
  * Hq query heads share Hkv KV heads, query head hq reading KV head
  * hq / (Hq / Hkv) (consecutive query heads form a group). The pools hold Hkv

@@ -249,3 +249,25 @@ def test_paged_prefill_varlen_rejects_bad_arguments(api):
     assert call(W=2049) == c["ATTN_ERR_UNSUPPORTED"]
     assert call(cu=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
     assert call(q=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+
+
+def test_paged_prefill_gqa_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+
+    def call(H=8, Hkv=2, q=FAKE, **kw):
+        a = dict(dict(B=2, total=40, maxq=30, D=128, nb=64, W=8), **kw)
+        return L.attn_paged_prefill_gqa(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, a["B"], H,
+                                        Hkv, a["total"], a["maxq"], a["D"], a["nb"], a["W"], 16,
+                                        1, 0.1, 1, None)
+
+    assert call(q=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(Hkv=3) == c["ATTN_ERR_BAD_SHAPE"]       # 3 does not divide 8
+    assert call(Hkv=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(D=96) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(q=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+
+
+def test_binding_exports_what_it_lists(api):
+    for name in api.__all__:
+        assert hasattr(api, name), name

@@ -423,6 +423,40 @@ def test_paged_prefill_varlen(api, lens, qlens, D, causal):
     assert e <= TOL_BF16 and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("group,D", [(4, 128), (8, 128), (2, 64)])
+def test_paged_prefill_gqa(api, group, D):
+    """Ragged chunked prefill over grouped-query pools (query head h reads KV
+    head h // group)."""
+    lens, qlens = (300, 1000, 77, 513), (300, 1, 77, 200)
+    inp = _paged(lens, 1, H=2, D=D, seed=97 + group)
+    g = torch.Generator().manual_seed(98)
+    q = torch.randn(sum(qlens), 2 * group, D, generator=g).to(torch.bfloat16)
+    say(f"gqa prefill group={group} D={D} lens={lens} qlens={qlens}")
+    o, lse, cu = _run_varlen(api, inp, qlens, q)
+    ref_o, ref_lse = oracle.paged_attention_varlen(q, cu, inp.k_pool, inp.v_pool,
+                                                   inp.block_tables, inp.seq_lens,
+                                                   1 / math.sqrt(D), True)
+    e, el = max_err(o, ref_o), lse_err(lse, ref_lse)
+    say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_paged_prefill_gqa_equals_repeated_kv_heads_bitwise(api):
+    """The grouped call gives the bits of the multi-head call on a pool whose
+    KV heads are repeated: the same kernel arithmetic, other K/V addresses."""
+    group = 4
+    inp = _paged((400, 900), 1, H=2, seed=99, poison=False)
+    g = torch.Generator().manual_seed(100)
+    qlens = [400, 130]
+    q = torch.randn(sum(qlens), 2 * group, 128, generator=g).to(torch.bfloat16)
+    o1, l1, _ = _run_varlen(api, inp, qlens, q)
+    rep = PagedInputs(inp.q, inp.k_pool.repeat_interleave(group, dim=1).contiguous(),
+                      inp.v_pool.repeat_interleave(group, dim=1).contiguous(), inp.block_tables,
+                      inp.seq_lens)
+    o2, l2, _ = _run_varlen(api, rep, qlens, q)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_paged_prefill_varlen_equal_lengths_bit_identical(api):
     """Equal query counts: the ragged call gives attn_paged_prefill's bits."""
     inp = _paged((300, 1000, 200), 200, H=2, seed=92)
