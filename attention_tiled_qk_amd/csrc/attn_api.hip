@@ -65,9 +65,11 @@ long long checked_mul(std::initializer_list<long long> xs) {
 // splits of about 32 blocks (512 tokens) on the longest possible sequence, so
 // that waves carry similar amounts of work whatever the length mix, raised
 // towards enough (split, head, sequence) waves to cover the chip several times
-// as long as every split keeps at least 4 blocks.
-int auto_splits(int B, int H, int max_blocks) {
-  long long s = (max_blocks + 31) / 32;
+// as long as every split keeps at least 4 blocks. Grouped-query waves write
+// `group` partial rows per split, so they take splits of about 64 blocks.
+int auto_splits(int B, int H, int max_blocks, int group) {
+  const int per = group > 1 ? 64 : 32;
+  long long s = (max_blocks + per - 1) / per;
   const long long waves = (long long)B * H;
   long long fill = (2048 + waves - 1) / waves;
   if (fill > max_blocks / 4) fill = max_blocks / 4;
@@ -133,8 +135,8 @@ namespace {
 
 // Split count the library uses for `Hkv` KV heads (one wave group per split, KV
 // head and sequence) when the caller passes num_splits = 0.
-int splits_for(int B, int Hkv, int max_blocks_per_seq, int num_splits) {
-  return num_splits == 0 ? auto_splits(B, Hkv, max_blocks_per_seq) : num_splits;
+int splits_for(int B, int Hkv, int group, int max_blocks_per_seq, int num_splits) {
+  return num_splits == 0 ? auto_splits(B, Hkv, max_blocks_per_seq, group) : num_splits;
 }
 
 size_t paged_workspace(int B, int Hq, int Hkv, int q_len, int D, int max_blocks_per_seq,
@@ -143,7 +145,8 @@ size_t paged_workspace(int B, int Hq, int Hkv, int q_len, int D, int max_blocks_
   if ((long long)(Hq / Hkv) * q_len > ATTN_PAGED_MAX_QLEN) return 0;
   if (D != 64 && D != 128) return 0;
   if (max_blocks_per_seq <= 0 || num_splits < 0 || num_splits > ATTN_PAGED_MAX_SPLITS) return 0;
-  return workspace_for(B, Hq, q_len, D, splits_for(B, Hkv, max_blocks_per_seq, num_splits));
+  return workspace_for(B, Hq, q_len, D,
+                       splits_for(B, Hkv, Hq / Hkv, max_blocks_per_seq, num_splits));
 }
 
 // k_scale == nullptr: bf16 pools; otherwise E4M3 pools (one byte per value)
@@ -176,7 +179,7 @@ int paged_decode(const void* q, const void* k_pool, const void* v_pool, const fl
   if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
     return ATTN_ERR_MISALIGNED;
   if (k_scale && (!aligned4(k_scale) || !aligned4(v_scale))) return ATTN_ERR_MISALIGNED;
-  const int S = splits_for(B, Hkv, max_blocks_per_seq, num_splits);
+  const int S = splits_for(B, Hkv, group, max_blocks_per_seq, num_splits);
   const size_t need = workspace_for(B, Hq, q_len, D, S);
   float* o_part = nullptr;
   float* lse_part = nullptr;
