@@ -11,6 +11,7 @@ stream the library launches on (torch's current stream, which the binding
 passes down).
 
 The same run also measures, under ``secondary``:
+  * c1: causal fp32 prefill B=1, H=1, L=128, D=64 (the correctness case; time only);
   * c3: causal bf16 prefill B=1, H=40, L=4096, D=128 (13B-style long prompt);
   * c4: paged decode, 64 sequences x 40 heads, q_len 1, lengths U[128, 4096];
   * c5: paged verify, 4 sequences x 40 heads, q_len 5, 32768 keys, shared
@@ -27,7 +28,7 @@ each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
-``--only NAME`` runs a single workload (c2, c3, c4, c5, c4g, cpf, append, c4f8, or ``copy``: a plain
+``--only NAME`` runs a single workload (c1, c2, c3, c4, c5, c4g, cpf, append, c4f8, or ``copy``: a plain
 device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
 its entry; that is the form the profiler runs use.
 
@@ -194,6 +195,21 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
             "launch_us_events": kernel_ms * 1e3,
         },
     }
+
+
+def bench_prefill_f32(torch, api, spec, warmup, steps):
+    """The fp32 correctness case: launch-latency bound, reported as time only."""
+    from workloads import prefill_inputs
+    q, k, v = (t.cuda() for t in prefill_inputs(spec))
+    o = torch.empty_like(q)
+    ms, wall = time_launches(torch, lambda: api.attn_prefill(q, k, v, causal=spec.causal,
+                                                             scale=spec.scale, o=o),
+                             warmup, steps)
+    flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
+    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/launch (events, binding included)")
+    return {"workload": spec.name, "ms_per_step": wall / steps, "launch_us_events": ms * 1e3,
+            "algorithmic_flops_per_launch": flops,
+            "note": "correctness configuration; launch-latency bound, time only"}
 
 
 def bench_paged(torch, api, spec, warmup, steps, key):
@@ -430,7 +446,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8", "copy"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8", "copy"],
                     help="run one workload and print its entry only")
     args = ap.parse_args()
 
@@ -446,10 +462,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import attention_tiled_qk_amd as api
-    from workloads import C2, C3, C4, C4F8, C4G, C5, CPF
+    from workloads import C1, C2, C3, C4, C4F8, C4G, C5, CPF
 
     steps, warmup = args.steps, args.warmup
     runners = {
+        "c1": lambda: bench_prefill_f32(torch, api, C1, warmup, steps),
         "c2": lambda: bench_prefill(torch, api, C2, warmup, steps, "prefill_c2"),
         "c3": lambda: bench_prefill(torch, api, C3, warmup, max(steps // 2, 3), "prefill_c3"),
         "c4": lambda: bench_paged(torch, api, C4, warmup, max(steps // 2, 3), "paged_c4"),
@@ -482,7 +499,7 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
-        "secondary": {name: runners[name]() for name in ("c3", "c4", "c5", "c4g", "cpf", "append", "c4f8")},
+        "secondary": {name: runners[name]() for name in ("c1", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8")},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
