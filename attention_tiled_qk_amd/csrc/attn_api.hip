@@ -42,7 +42,7 @@ namespace {
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
 constexpr int kPrefillRowsBf16 = 128;  // query rows per prefill workgroup (bf16)
-constexpr int kPrefillRowsF32 = 64;
+constexpr int kPrefillRowsF32 = 8;
 constexpr int kMaxMergeSplits = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

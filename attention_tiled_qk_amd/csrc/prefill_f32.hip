@@ -4,16 +4,18 @@
 // §2.2, K/V tiles staged in LDS, running max m and exp-sum l per row, one
 // division by l after the last tile -- computed in float32 on the vector ALUs
 // with accurate expf, because float32 inputs are held to a 1e-5 bound that
-// bf16 matrix-core operands cannot meet. Each query row is owned by two lanes
-// (one half of the head dimension each); a workgroup covers 64 rows and walks
-// 32-key tiles.
+// bf16 matrix-core operands cannot meet. Each query row is owned by sixteen
+// lanes (a sixteenth of the head dimension each, partial dot products summed
+// by a shuffle tree); a workgroup covers 8 rows and walks 32-key tiles, so
+// even a short sequence spreads over several CUs.
 #include "common.h"
 
 namespace attn {
 
 namespace {
-constexpr int F_BM = 64;  // query rows per workgroup
-constexpr int F_BN = 32;  // keys per tile
+constexpr int F_LPR = 16;            // lanes per query row
+constexpr int F_BM = 128 / F_LPR;    // query rows per workgroup (128 threads)
+constexpr int F_BN = 32;             // keys per tile
 }  // namespace
 
 template <int D, bool CAUSAL>
@@ -23,22 +25,22 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
                                                           float* __restrict__ o,
                                                           float* __restrict__ lse, int L,
                                                           int n_qtiles, float scale) {
-  constexpr int HD = D / 2;
+  constexpr int HD = D / F_LPR;
   constexpr int PITCH = D + 4;
   __shared__ float ks[F_BN * PITCH];
   __shared__ float vs[F_BN * PITCH];
 
   const int tid = threadIdx.x;
-  const int half = tid & 1;
+  const int slice = tid % F_LPR;  // which slice of the head dimension this lane holds
   const int bh = blockIdx.x / n_qtiles;
   const int qt = blockIdx.x % n_qtiles;
-  const int row = qt * F_BM + (tid >> 1);
+  const int row = qt * F_BM + tid / F_LPR;
   const size_t head_off = (size_t)bh * L * D;
 
   float qr[HD], acc[HD];
 #pragma unroll
   for (int d = 0; d < HD; ++d) {
-    qr[d] = row < L ? q[head_off + (size_t)row * D + half * HD + d] : 0.f;
+    qr[d] = row < L ? q[head_off + (size_t)row * D + slice * HD + d] : 0.f;
     acc[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -62,8 +64,10 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
     for (int j = 0; j < F_BN; ++j) {
       float part = 0.f;
 #pragma unroll
-      for (int d = 0; d < HD; ++d) part = __builtin_fmaf(qr[d], ks[j * PITCH + half * HD + d], part);
-      const float full = part + __shfl_xor(part, 1);
+      for (int d = 0; d < HD; ++d) part = __builtin_fmaf(qr[d], ks[j * PITCH + slice * HD + d], part);
+      float full = part;
+#pragma unroll
+      for (int x = 1; x < F_LPR; x <<= 1) full += __shfl_xor(full, x);
       const int key = kt * F_BN + j;
       const bool vis = key < L && (!CAUSAL || key <= row);
       s[j] = vis ? full * scale : -INFINITY;
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
         const float p = s[j] == -INFINITY ? 0.f : expf(s[j] - m_new);
         l += p;
 #pragma unroll
-        for (int d = 0; d < HD; ++d) acc[d] = __builtin_fmaf(p, vs[j * PITCH + half * HD + d], acc[d]);
+        for (int d = 0; d < HD; ++d) acc[d] = __builtin_fmaf(p, vs[j * PITCH + slice * HD + d], acc[d]);
       }
       m = m_new;
     }
@@ -89,8 +93,8 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
   if (row < L) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) o[head_off + (size_t)row * D + half * HD + d] = acc[d] * inv;
-    if (lse != nullptr && half == 0) lse[(size_t)bh * L + row] = l > 0.f ? m + logf(l) : -INFINITY;
+    for (int d = 0; d < HD; ++d) o[head_off + (size_t)row * D + slice * HD + d] = acc[d] * inv;
+    if (lse != nullptr && slice == 0) lse[(size_t)bh * L + row] = l > 0.f ? m + logf(l) : -INFINITY;
   }
 }
 
