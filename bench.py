@@ -184,7 +184,7 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
         "ms_per_step": wall / steps,
         "value": flops / (wall / steps * 1e-3) / 1e12,
         "roofline": {
-            "kernel": f"prefill_bf16_kernel<{spec.D}, causal={int(spec.causal)}>",
+            "kernel": f"prefill_bf16_pipe_kernel<{spec.D}, 4, 64, causal={int(spec.causal)}>",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
