@@ -184,16 +184,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // Per-lane source offsets of the tile loads: relative to the tile (dense) or
   // to the piece's first row (paged: a piece's RPP rows are consecutive slots of
-  // one cache block, contiguous in the pool).
-  unsigned koff[C::PPW], voff[C::PPW];
-#pragma unroll
-  for (int i = 0; i < C::PPW; ++i) {
-    const int piece = wave + NW * i;
-    const int row = piece * C::RPP + lane / C::NCH;
+  // one cache block, contiguous in the pool). Piece i of this wave starts
+  // NW * RPP rows (4096 bytes) after piece i - 1 and both swizzles repeat every
+  // 16 rows, so one offset per lane serves every piece, each piece having a buffer
+  // descriptor of its own.
+  static_assert(NW * C::RPP * C::ROWB == 4096, "piece stride");
+  unsigned koff, voff;
+  {
+    const int row = wave * C::RPP + lane / C::NCH;
     const int phys = lane % C::NCH;
     const int base = PAGED ? (lane / C::NCH) * C::ROWB : row * C::ROWB;
-    koff[i] = base + (phys ^ kswz<C::NCH>(row)) * 16;
-    voff[i] = base + (phys ^ vswz<C::NCH>(row)) * 16;
+    koff = base + (phys ^ kswz<C::NCH>(row)) * 16;
+    voff = base + (phys ^ vswz<C::NCH>(row)) * 16;
   }
   if constexpr (PAGED) {
     // stage this sequence's block ids once; reading them back from LDS keeps
@@ -221,41 +223,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bf16* src = pool + (((size_t)blk * pg.kv_heads + kvh) * 16 + (key & 15)) * D;
     return buffer_rsrc(src, min(C::RPP, Lk - key) * C::ROWB);
   };
+  // Dense source of piece i of tile kt: rows kt * BN + NW * RPP * i onwards,
+  // bounded by the head's L rows so that the ragged tail reads zeros.
+  auto dense_piece = [&](const bf16* head, int kt, int i) -> __amdgpu_buffer_rsrc_t {
+    const int row0 = kt * BN + NW * C::RPP * i;
+    return buffer_rsrc(head + (size_t)row0 * D, max(L - row0, 0) * C::ROWB);
+  };
   auto issue_k = [&](auto s, int kt) {
     if constexpr (PAGED) {
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i), kst(s) + (wave + NW * i) * 1024, koff[i]);
+      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i), kst(s) + (wave + NW * i) * 1024, koff);
     } else {
-      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(r, kst(s) + (wave + NW * i) * 1024, koff[i]);
+      for (int i = 0; i < C::PPW; ++i) dma16(dense_piece(kh, kt, i), kst(s) + (wave + NW * i) * 1024, koff);
     }
   };
   auto issue_v = [&](auto s, int kt) {
     if constexpr (PAGED) {
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i), vst(s) + (wave + NW * i) * 1024, voff[i]);
+      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i), vst(s) + (wave + NW * i) * 1024, voff);
     } else {
-      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vh + (size_t)kt * BN * D, (L - kt * BN) * C::ROWB);
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(r, vst(s) + (wave + NW * i) * 1024, voff[i]);
+      for (int i = 0; i < C::PPW; ++i) dma16(dense_piece(vh, kt, i), vst(s) + (wave + NW * i) * 1024, voff);
     }
   };
 
-  int kaddr[C::KC];
-#pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc)
-    kaddr[kc] = l32 * C::ROWB + (((2 * kc + g) ^ kswz<C::NCH>(l32)) * 16);
-  int vaddr[C::DB];
+  // LDS operand addresses. Chunk 2 kc + g of K row l32 sits at chunk
+  // (2 kc + g) ^ kswz(l32) = (2 kc) ^ (g ^ kswz(l32)), so the address of k-chunk
+  // kc is that of chunk 0 XOR 32 kc; likewise V column block db is block 0
+  // XOR 64 db. One register each instead of one per chunk.
+  const int kaddr0 = l32 * C::ROWB + ((g ^ kswz<C::NCH>(l32)) * 16);
+  int vaddr0;
   {
     const int i16 = lane & 15;
     const int grp = lane >> 4;
     const int r = 4 * g + (i16 >> 2);
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int c = db * 4 + 2 * (grp & 1) + ((i16 & 3) >> 1);
-      vaddr[db] = r * C::ROWB + ((c ^ vswz<C::NCH>(r)) * 16) + 8 * (i16 & 1);
-    }
+    const int c = 2 * (grp & 1) + ((i16 & 3) >> 1);
+    vaddr0 = r * C::ROWB + ((c ^ vswz<C::NCH>(r)) * 16) + 8 * (i16 & 1);
   }
 
   const bool neg = scale < 0.f;
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       sc[kb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kb_ + kaddr[kc] + kb * 32 * C::ROWB);
+        const bf16x8 a = *reinterpret_cast<const ATTN_LDS bf16x8*>(kb_ + (kaddr0 ^ (32 * kc)) + kb * 32 * C::ROWB);
         sc[kb] = mfma32(a, qreg[kc], sc[kb]);
       }
     }
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int cidx = 0; cidx < 2 * C::NKB; ++cidx) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const ATTN_LDS unsigned char* base = vb_ + vaddr[db] + cidx * 16 * C::ROWB;
+        const ATTN_LDS unsigned char* base = vb_ + (vaddr0 ^ (64 * db)) + cidx * 16 * C::ROWB;
         const bf16x4 lo = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base));
         const bf16x4 hi = lds_read_tr(reinterpret_cast<const ATTN_LDS bf16x4*>(base + 8 * C::ROWB));
         acc[db] = mfma32(join(lo, hi), p[cidx], acc[db]);
