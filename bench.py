@@ -137,13 +137,15 @@ def cpu_baseline(spec, budget_s):
         done_per_pass.append(done)
         walls.append(dt)
     cores = len(os.sched_getaffinity(0))
+    lo, hi = min(done_per_pass), max(done_per_pass)
+    span = f"{lo}" if lo == hi else f"{lo}-{hi}"
     return {
         "value": statistics.median(rates),
         "unit": "TFLOP/s",
         "cores": blas_threads if blas_threads else cores,
         "host_cores": cores,
         "kind": "oracle",
-        "sample": f"median of 3 passes over {min(done_per_pass)}-{max(done_per_pass)} of the "
+        "sample": f"median of 3 passes over {span} of the "
                   f"{len(pairs)} (batch, head) pairs of the c2 workload, float64, "
                   f"{sum(walls):.1f} s wall in all; the rate counts the same algorithmic (causal) "
                   f"FLOPs as the GPU although the oracle computes every pair of the square",
