@@ -22,7 +22,8 @@ __all__ = [
     "attn_paged_prefill_varlen", "attn_paged_prefill_gqa",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
     "KVCacheAllocator", "attn_paged_append_fp8", "attn_paged_copy_blocks_fp8",
-    "attn_paged_decode_fp8", "attn_version", "lib", "LIB_PATH", "ATTN_F32", "ATTN_BF16",
+    "attn_paged_decode_fp8", "attn_probe_block_read", "attn_version", "lib", "LIB_PATH",
+    "ATTN_F32", "ATTN_BF16",
 ]
 
 ATTN_F32 = 0
@@ -65,6 +66,8 @@ lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_gather.restype = _i
+lib.attn_probe_block_read.argtypes = [_p, _i, _i, _p, _i, _p, _i, _p]
+lib.attn_probe_block_read.restype = _i
 lib.attn_paged_append.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_append.restype = _i
 lib.attn_paged_copy_blocks.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
@@ -365,6 +368,25 @@ def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, st
                                nblk, width, max_seq_len, _stream(pool.device, stream))
     _check(st, "attn_paged_gather")
     return out
+
+
+def attn_probe_block_read(buf, block_bytes, order, n_waves, *, sink=None, stream=None):
+    """Read the blocks of buf (uint8, a multiple of block_bytes long) listed in
+    order (int32) and nothing else; returns sink [n_waves * 64] int32 whose XOR
+    over all words is the XOR of every 32-bit word read. A bandwidth probe."""
+    _dev(buf, "buf", torch.uint8)
+    _dev(order, "order", torch.int32)
+    if buf.numel() % block_bytes != 0:
+        raise ValueError("buf must hold a whole number of blocks")
+    if sink is None:
+        sink = torch.empty(n_waves * 64, device=buf.device, dtype=torch.int32)
+    _dev(sink, "sink", torch.int32)
+    if sink.numel() < n_waves * 64:
+        raise ValueError("sink must hold n_waves * 64 words")
+    st = lib.attn_probe_block_read(_ptr(buf), buf.numel() // block_bytes, block_bytes, _ptr(order),
+                                   order.numel(), _ptr(sink), n_waves, _stream(buf.device, stream))
+    _check(st, "attn_probe_block_read")
+    return sink
 
 
 def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, stream=None):

@@ -24,13 +24,16 @@ The same run also measures, under ``secondary``:
     (attn_paged_append), priced against HBM bandwidth;
   * c4f8: the c4 decode over an FP8 (E4M3) cache with per-(block, head)
     scales (attn_paged_decode_fp8): one byte per cached value;
-each with its own roofline entry (MFMA TFLOP/s or HBM GB/s). The
+each with its own roofline entry (MFMA TFLOP/s or HBM GB/s); and
+  * probe: the read bandwidth HBM sustains for the paged kernels' access
+    patterns -- 4 KiB and 2 KiB blocks of a 2.5 GiB buffer in random order,
+    and 4 KiB blocks in address order (attn_probe_block_read, loads only). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
-``--only NAME`` runs a single workload (c1, c2, c3, c4, c5, c4g, cpf, append, c4f8, or ``copy``: a plain
-device-to-device copy of 2 GiB used to calibrate HBM byte counters) and prints
-its entry; that is the form the profiler runs use.
+``--only NAME`` runs a single workload (c1, c2, c3, c4, c5, c4g, cpf, append, c4f8, probe, or
+``copy``: a plain device-to-device copy of 2 GiB used to calibrate HBM byte
+counters) and prints its entry; that is the form the profiler runs use.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
 """
@@ -451,6 +454,34 @@ def bench_copy(torch, warmup, steps):
             "ms_per_step": wall / steps, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}
 
 
+def bench_probe(torch, api, warmup, steps):
+    """Read-bandwidth ceilings of the paged kernels' access patterns: whole
+    blocks of a 2.5 GiB buffer read in a random order -- 4 KiB, one bf16 cache
+    slab of a (block, head) at D = 128, and 2 KiB, one FP8 slab -- and in
+    address order, through attn_probe_block_read (loads only, 8192 waves)."""
+    total = 5 << 29
+    buf = torch.zeros(total, dtype=torch.uint8, device="cuda")
+    g = torch.Generator().manual_seed(12)
+    n_waves = 8192
+    sink = torch.empty(n_waves * 64, dtype=torch.int32, device="cuda")
+    res = {"workload": "read_probe_2.5GiB",
+           "note": "bytes read / time; the ceiling the paged kernels' block reads can reach"}
+    for name, bb, shuffled in (("random_4KiB", 4096, True), ("random_2KiB", 2048, True),
+                               ("linear_4KiB", 4096, False)):
+        n = total // bb
+        ids = torch.randperm(n, generator=g) if shuffled else torch.arange(n)
+        order = ids.to(torch.int32).cuda()
+        ms, _ = time_launches(
+            torch, lambda: api.attn_probe_block_read(buf, bb, order, n_waves, sink=sink), warmup, steps)
+        gbs = total / (ms * 1e-3) / 1e9
+        log(f"[bench] read probe {name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})")
+        res[name] = {"GBps": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, "launch_us_events": ms * 1e3}
+        del order
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,7 +489,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8", "copy"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8", "copy",
+                                       "probe"],
                     help="run one workload and print its entry only")
     args = ap.parse_args()
 
@@ -488,6 +520,7 @@ def main():
         "append": lambda: bench_append(torch, api, CPF, warmup, max(steps // 2, 3), "append_cpf"),
         "c4f8": lambda: bench_paged_fp8(torch, api, C4F8, warmup, max(steps // 2, 3), "paged_c4f8"),
         "copy": lambda: bench_copy(torch, warmup, steps),
+        "probe": lambda: bench_probe(torch, api, 3, 20),
     }
     if args.only:
         print(json.dumps({"only": args.only, **runners[args.only]()}), flush=True)
@@ -511,7 +544,8 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
-        "secondary": {name: runners[name]() for name in ("c1", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8")},
+        "secondary": {name: runners[name]() for name in ("c1", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8",
+                                                         "probe")},
     }
     if args.cpu_seconds > 0:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")

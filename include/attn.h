@@ -452,6 +452,31 @@ int attn_paged_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
                           int block_size, int causal, float scale, int num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_probe_block_read -- diagnostic: read whole blocks of a device buffer in
+ * a given order and compute nothing else, to measure the read bandwidth HBM
+ * sustains for an access pattern: the ceiling of the memory-bound paged
+ * kernels, in the sense of the roofline of [P4] (scattered 2 and 4 KiB cache
+ * slabs sustain less than streaming reads).
+ *
+ *   buf         : num_blocks * block_bytes bytes of device memory, 16-byte
+ *                 aligned.
+ *   block_bytes : 1024, 2048, 4096, 8192 or 16384.
+ *   order       : [n_reads] int32 device: the block ids to read, each in
+ *                 [0, num_blocks) (not checked on the device: an id outside is
+ *                 undefined behaviour, as for block tables).
+ *   sink        : [n_waves * 64] uint32 device, written: lane l of wave w
+ *                 stores the XOR of the 32-bit words it read, so the XOR of
+ *                 all sink words equals the XOR of every word of every block
+ *                 read (each entry of order counted once).
+ *   n_waves     : waves launched, a multiple of 4 in [4, 2^22]; wave w reads
+ *                 order[w], order[w + n_waves], ..., two blocks at a time, 16
+ *                 bytes per lane per load.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_probe_block_read(const void* buf, int num_blocks, int block_bytes, const int32_t* order,
+                          int n_reads, uint32_t* sink, int n_waves, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_string(int status);
 

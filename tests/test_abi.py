@@ -187,6 +187,27 @@ def test_merge_and_gather_reject_bad_arguments(api):
     assert L.attn_paged_gather(FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 4, 4, 0, None) == c["ATTN_ERR_BAD_SHAPE"]
 
 
+def test_probe_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+
+    def call(buf=FAKE, nb=64, bb=4096, order=FAKE, n=64, sink=FAKE, waves=8):
+        return L.attn_probe_block_read(buf, nb, bb, order, n, sink, waves, None)
+
+    assert call(buf=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(order=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(sink=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(nb=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(n=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(bb=3072) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(bb=32768) == c["ATTN_ERR_UNSUPPORTED"]
+    assert call(waves=6) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(waves=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(waves=1 << 23) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(buf=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
+    assert call(order=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
+
+
 def test_binding_refuses_cpu_tensors(api):
     import torch
     x = torch.zeros(1, 1, 4, 64)
