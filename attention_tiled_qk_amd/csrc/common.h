@@ -87,6 +87,15 @@ __device__ __forceinline__ bf16x8 join(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 16-byte load of data that is read once (global_load_dwordx4 ... nt): the
+// caches hold it at streaming priority. For scattered 2-4 KiB block reads this
+// draws about 11% more HBM bandwidth than the default policy (measured; for
+// the contiguous rows of the append kernel it is slower, so only the paged
+// attention kernels use it).
+__device__ __forceinline__ u32x4 load_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw (unformatted) buffer descriptor, gfx9
 
 // Buffer descriptor over [base, base + bytes): reads past the end return zero.

@@ -181,9 +181,9 @@ void paged_attn_kernel(
       const uint8_t* va_src = v_pool + (size_t)pa * blk_stride + head_off;
 #pragma unroll
       for (int i = 0; i < KR; ++i)
-        r.ka[i] = *reinterpret_cast<const u32x4*>(ka_src + l16 * D + g * (D / 4) + 16 * i);
+        r.ka[i] = load_stream(ka_src + l16 * D + g * (D / 4) + 16 * i);
 #pragma unroll
-      for (int i = 0; i < VR; ++i) r.va[i] = *reinterpret_cast<const u32x4*>(va_src + (i * 64 + lane) * 16);
+      for (int i = 0; i < VR; ++i) r.va[i] = load_stream(va_src + (i * 64 + lane) * 16);
       r.ska = k_scale[(size_t)pa * H + h];
       r.sva = v_scale[(size_t)pa * H + h];
       if (has_b) {
@@ -192,9 +192,9 @@ void paged_attn_kernel(
         const uint8_t* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
 #pragma unroll
         for (int i = 0; i < KR; ++i)
-          r.kb[i] = *reinterpret_cast<const u32x4*>(kb_src + l16 * D + g * (D / 4) + 16 * i);
+          r.kb[i] = load_stream(kb_src + l16 * D + g * (D / 4) + 16 * i);
 #pragma unroll
-        for (int i = 0; i < VR; ++i) r.vb[i] = *reinterpret_cast<const u32x4*>(vb_src + (i * 64 + lane) * 16);
+        for (int i = 0; i < VR; ++i) r.vb[i] = load_stream(vb_src + (i * 64 + lane) * 16);
         r.skb = k_scale[(size_t)pb * H + h];
         r.svb = v_scale[(size_t)pb * H + h];
       } else {
@@ -210,18 +210,18 @@ void paged_attn_kernel(
     const bf16* va_src = v_pool + (size_t)pa * blk_stride + head_off;
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-      r.ka[c] = *reinterpret_cast<const bf16x8*>(ka_src + l16 * D + 32 * c + 8 * g);
+      r.ka[c] = __builtin_bit_cast(bf16x8, load_stream(ka_src + l16 * D + 32 * c + 8 * g));
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) r.va[i] = *reinterpret_cast<const u32x4*>(va_src + (i * 64 + lane) * 8);
+    for (int i = 0; i < VCH; ++i) r.va[i] = load_stream(va_src + (i * 64 + lane) * 8);
     if (has_b) {
       const int pb = block_id(n + 1);
       const bf16* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
       const bf16* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
 #pragma unroll
       for (int c = 0; c < DC; ++c)
-        r.kb[c] = *reinterpret_cast<const bf16x8*>(kb_src + l16 * D + 32 * c + 8 * g);
+        r.kb[c] = __builtin_bit_cast(bf16x8, load_stream(kb_src + l16 * D + 32 * c + 8 * g));
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) r.vb[i] = *reinterpret_cast<const u32x4*>(vb_src + (i * 64 + lane) * 8);
+      for (int i = 0; i < VCH; ++i) r.vb[i] = load_stream(vb_src + (i * 64 + lane) * 8);
     } else {
 #pragma unroll
       for (int c = 0; c < DC; ++c) r.kb[c] = bf16x8{};
