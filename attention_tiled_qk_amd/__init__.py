@@ -66,7 +66,7 @@ lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_gather.restype = _i
-lib.attn_probe_block_read.argtypes = [_p, _i, _i, _p, _i, _p, _i, _p]
+lib.attn_probe_block_read.argtypes = [_p, _i, _i, _p, _i, _p, _i, _i, _p]
 lib.attn_probe_block_read.restype = _i
 lib.attn_paged_append.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_append.restype = _i
@@ -370,10 +370,12 @@ def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, st
     return out
 
 
-def attn_probe_block_read(buf, block_bytes, order, n_waves, *, sink=None, stream=None):
+def attn_probe_block_read(buf, block_bytes, order, n_waves, *, nontemporal=False, sink=None,
+                          stream=None):
     """Read the blocks of buf (uint8, a multiple of block_bytes long) listed in
-    order (int32) and nothing else; returns sink [n_waves * 64] int32 whose XOR
-    over all words is the XOR of every 32-bit word read. A bandwidth probe."""
+    order (int32) and nothing else, with the default or the nontemporal cache
+    policy; returns sink [n_waves * 64] int32 whose XOR over all words is the
+    XOR of every 32-bit word read. A bandwidth probe."""
     _dev(buf, "buf", torch.uint8)
     _dev(order, "order", torch.int32)
     if buf.numel() % block_bytes != 0:
@@ -384,7 +386,8 @@ def attn_probe_block_read(buf, block_bytes, order, n_waves, *, sink=None, stream
     if sink.numel() < n_waves * 64:
         raise ValueError("sink must hold n_waves * 64 words")
     st = lib.attn_probe_block_read(_ptr(buf), buf.numel() // block_bytes, block_bytes, _ptr(order),
-                                   order.numel(), _ptr(sink), n_waves, _stream(buf.device, stream))
+                                   order.numel(), _ptr(sink), n_waves, int(bool(nontemporal)),
+                                   _stream(buf.device, stream))
     _check(st, "attn_probe_block_read")
     return sink
 

@@ -36,7 +36,7 @@ hipError_t launch_paged_append_fp8(const void*, const void*, void*, void*, float
                                    hipStream_t);
 hipError_t launch_paged_copy_blocks_fp8(void*, void*, float*, float*, const int32_t*,
                                         const int32_t*, int, int, int, hipStream_t);
-hipError_t launch_probe_block_read(const void*, int, const int32_t*, int, uint32_t*, int,
+hipError_t launch_probe_block_read(const void*, int, const int32_t*, int, uint32_t*, int, int,
                                    hipStream_t);
 }  // namespace attn
 
@@ -351,16 +351,19 @@ int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32
 }
 
 int attn_probe_block_read(const void* buf, int num_blocks, int block_bytes, const int32_t* order,
-                          int n_reads, uint32_t* sink, int n_waves, void* stream) {
+                          int n_reads, uint32_t* sink, int n_waves, int nontemporal,
+                          void* stream) {
   if (!buf || !order || !sink) return ATTN_ERR_NULL_PTR;
   if (num_blocks <= 0 || n_reads <= 0) return ATTN_ERR_BAD_SHAPE;
   if (block_bytes != 1024 && block_bytes != 2048 && block_bytes != 4096 && block_bytes != 8192 &&
       block_bytes != 16384)
     return ATTN_ERR_UNSUPPORTED;
   if (n_waves < 4 || n_waves > (1 << 22) || n_waves % 4 != 0) return ATTN_ERR_BAD_SHAPE;
+  if (nontemporal != 0 && nontemporal != 1) return ATTN_ERR_BAD_SHAPE;
   if (!aligned16(buf)) return ATTN_ERR_MISALIGNED;
   if (!aligned4(order) || !aligned4(sink)) return ATTN_ERR_MISALIGNED;
   return hip_status(attn::launch_probe_block_read(buf, block_bytes, order, n_reads, sink, n_waves,
+                                                  nontemporal,
                                                   reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -27,7 +27,9 @@ The same run also measures, under ``secondary``:
 each with its own roofline entry (MFMA TFLOP/s or HBM GB/s); and
   * probe: the read bandwidth HBM sustains for the paged kernels' access
     patterns -- 4 KiB and 2 KiB blocks of a 2.5 GiB buffer in random order,
-    and 4 KiB blocks in address order (attn_probe_block_read, loads only). The
+    and 4 KiB blocks in address order (attn_probe_block_read, loads only,
+    nontemporal like the paged kernels; random 4 KiB also with the default
+    cache policy). The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
@@ -458,7 +460,9 @@ def bench_probe(torch, api, warmup, steps):
     """Read-bandwidth ceilings of the paged kernels' access patterns: whole
     blocks of a 2.5 GiB buffer read in a random order -- 4 KiB, one bf16 cache
     slab of a (block, head) at D = 128, and 2 KiB, one FP8 slab -- and in
-    address order, through attn_probe_block_read (loads only, 8192 waves)."""
+    address order, through attn_probe_block_read (loads only, 8192 waves),
+    with nontemporal loads (the policy of the paged kernels) and, for the
+    random 4 KiB case, the default policy too."""
     total = 5 << 29
     buf = torch.zeros(total, dtype=torch.uint8, device="cuda")
     g = torch.Generator().manual_seed(12)
@@ -466,13 +470,16 @@ def bench_probe(torch, api, warmup, steps):
     sink = torch.empty(n_waves * 64, dtype=torch.int32, device="cuda")
     res = {"workload": "read_probe_2.5GiB",
            "note": "bytes read / time; the ceiling the paged kernels' block reads can reach"}
-    for name, bb, shuffled in (("random_4KiB", 4096, True), ("random_2KiB", 2048, True),
-                               ("linear_4KiB", 4096, False)):
+    for name, bb, shuffled, nt in (("random_4KiB_nt", 4096, True, True),
+                                   ("random_2KiB_nt", 2048, True, True),
+                                   ("linear_4KiB_nt", 4096, False, True),
+                                   ("random_4KiB_default", 4096, True, False)):
         n = total // bb
         ids = torch.randperm(n, generator=g) if shuffled else torch.arange(n)
         order = ids.to(torch.int32).cuda()
         ms, _ = time_launches(
-            torch, lambda: api.attn_probe_block_read(buf, bb, order, n_waves, sink=sink), warmup, steps)
+            torch, lambda: api.attn_probe_block_read(buf, bb, order, n_waves, nontemporal=nt, sink=sink),
+            warmup, steps)
         gbs = total / (ms * 1e-3) / 1e9
         log(f"[bench] read probe {name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})")
         res[name] = {"GBps": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, "launch_us_events": ms * 1e3}

@@ -472,10 +472,13 @@ int attn_paged_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
  *   n_waves     : waves launched, a multiple of 4 in [4, 2^22]; wave w reads
  *                 order[w], order[w + n_waves], ..., two blocks at a time, 16
  *                 bytes per lane per load.
+ *   nontemporal : 0 = default cache policy, 1 = nontemporal loads (the policy
+ *                 the paged attention kernels use for the cache).
  * Returns ATTN_OK or a negative ATTN_ERR_* code.
  */
 int attn_probe_block_read(const void* buf, int num_blocks, int block_bytes, const int32_t* order,
-                          int n_reads, uint32_t* sink, int n_waves, void* stream);
+                          int n_reads, uint32_t* sink, int n_waves, int nontemporal,
+                          void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_string(int status);

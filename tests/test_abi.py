@@ -191,8 +191,8 @@ def test_probe_rejects_bad_arguments(api):
     c = header_constants()
     L = api.lib
 
-    def call(buf=FAKE, nb=64, bb=4096, order=FAKE, n=64, sink=FAKE, waves=8):
-        return L.attn_probe_block_read(buf, nb, bb, order, n, sink, waves, None)
+    def call(buf=FAKE, nb=64, bb=4096, order=FAKE, n=64, sink=FAKE, waves=8, nt=0):
+        return L.attn_probe_block_read(buf, nb, bb, order, n, sink, waves, nt, None)
 
     assert call(buf=None) == c["ATTN_ERR_NULL_PTR"]
     assert call(order=None) == c["ATTN_ERR_NULL_PTR"]
@@ -204,6 +204,7 @@ def test_probe_rejects_bad_arguments(api):
     assert call(waves=6) == c["ATTN_ERR_BAD_SHAPE"]
     assert call(waves=0) == c["ATTN_ERR_BAD_SHAPE"]
     assert call(waves=1 << 23) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(nt=2) == c["ATTN_ERR_BAD_SHAPE"]
     assert call(buf=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
     assert call(order=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
 
