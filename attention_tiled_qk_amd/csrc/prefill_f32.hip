@@ -6,8 +6,10 @@
 // with accurate expf, because float32 inputs are held to a 1e-5 bound that
 // bf16 matrix-core operands cannot meet. Each query row is owned by sixteen
 // lanes (a sixteenth of the head dimension each, partial dot products summed
-// by a shuffle tree); a workgroup covers 8 rows and walks 32-key tiles, so
-// even a short sequence spreads over several CUs.
+// by a shuffle tree); a workgroup covers 8 rows and walks 32- or 64-key tiles, so
+// even a short sequence spreads over several CUs. Tiles arrive with 16-byte
+// loads into registers one tile ahead: the loads of tile j+1 are in flight
+// while tile j is computed, and reach LDS after the next barrier.
 #include "common.h"
 
 namespace attn {
@@ -15,7 +17,9 @@ namespace attn {
 namespace {
 constexpr int F_LPR = 16;            // lanes per query row
 constexpr int F_BM = 128 / F_LPR;    // query rows per workgroup (128 threads)
-constexpr int F_BN = 32;             // keys per tile
+// keys per tile: 64 at D = 64 (fewer barriers and load round trips), 32 at
+// D = 128, where the registers staging a 64-key tile would not fit
+constexpr int f32_tile_keys(int D) { return D == 64 ? 64 : 32; }
 }  // namespace
 
 template <int D, bool CAUSAL>
@@ -25,10 +29,11 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
                                                           float* __restrict__ o,
                                                           float* __restrict__ lse, int L,
                                                           int n_qtiles, float scale) {
+  constexpr int F_BN = f32_tile_keys(D);
   constexpr int HD = D / F_LPR;
   constexpr int PITCH = D + 4;
-  __shared__ float ks[F_BN * PITCH];
-  __shared__ float vs[F_BN * PITCH];
+  __shared__ __attribute__((aligned(16))) float ks[F_BN * PITCH];
+  __shared__ __attribute__((aligned(16))) float vs[F_BN * PITCH];
 
   const int tid = threadIdx.x;
   const int slice = tid % F_LPR;  // which slice of the head dimension this lane holds
@@ -48,15 +53,34 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
   const int n_all = (L + F_BN - 1) / F_BN;
   const int n_kt = CAUSAL ? min(n_all, (min(qt * F_BM + F_BM, L) - 1) / F_BN + 1) : n_all;
 
+  // 16-byte piece u of this thread: tile row (tid + 128 u) / (D / 4), column
+  // 4 ((tid + 128 u) % (D / 4)); keys past L read as zeros
+  constexpr int C4 = D / 4;
+  constexpr int VEC = F_BN * C4 / 128;
+  f32x4 kreg[VEC], vreg[VEC];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      const int i4 = tid + 128 * u;
+      const int key = kt * F_BN + i4 / C4;
+      const size_t at = head_off + (size_t)key * D + 4 * (i4 % C4);
+      kreg[u] = key < L ? *reinterpret_cast<const f32x4*>(k + at) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vreg[u] = key < L ? *reinterpret_cast<const f32x4*>(v + at) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  fetch(0);
+
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    for (int i = tid; i < F_BN * D; i += 128) {
-      const int r = i / D, d = i % D;
-      const int key = kt * F_BN + r;
-      ks[r * PITCH + d] = key < L ? k[head_off + (size_t)key * D + d] : 0.f;
-      vs[r * PITCH + d] = key < L ? v[head_off + (size_t)key * D + d] : 0.f;
+    __syncthreads();  // every lane is done reading the previous tile
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      const int i4 = tid + 128 * u;
+      const int at = (i4 / C4) * PITCH + 4 * (i4 % C4);
+      *reinterpret_cast<f32x4*>(ks + at) = kreg[u];
+      *reinterpret_cast<f32x4*>(vs + at) = vreg[u];
     }
     __syncthreads();
+    if (kt + 1 < n_kt) fetch(kt + 1);
 
     float s[F_BN];
     float mt = -INFINITY;
