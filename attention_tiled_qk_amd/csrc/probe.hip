@@ -14,7 +14,7 @@
 namespace attn {
 
 template <bool NT>
-__device__ __forceinline__ u32x4 load(const u32x4* p) {
+__device__ __forceinline__ u32x4 probe_load(const u32x4* p) {
   if constexpr (NT) return load_stream(p);
   else return *p;
 }
@@ -33,16 +33,16 @@ __global__ __launch_bounds__(256) void block_read_kernel(const u32x4* __restrict
     const u32x4* b = buf + (size_t)order[i + n_waves] * CH * 64;
     u32x4 va[CH], vb[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) va[c] = load<NT>(a + c * 64 + lane);
+    for (int c = 0; c < CH; ++c) va[c] = probe_load<NT>(a + c * 64 + lane);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) vb[c] = load<NT>(b + c * 64 + lane);
+    for (int c = 0; c < CH; ++c) vb[c] = probe_load<NT>(b + c * 64 + lane);
 #pragma unroll
     for (int c = 0; c < CH; ++c) acc ^= va[c] ^ vb[c];
   }
   if (i < n_reads) {
     const u32x4* a = buf + (size_t)order[i] * CH * 64;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) acc ^= load<NT>(a + c * 64 + lane);
+    for (int c = 0; c < CH; ++c) acc ^= probe_load<NT>(a + c * 64 + lane);
   }
   sink[(size_t)wave * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
