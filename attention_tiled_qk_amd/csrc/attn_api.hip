@@ -181,7 +181,15 @@ int paged_decode(const void* q, const void* k_pool, const void* v_pool, const fl
   if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
     return ATTN_ERR_MISALIGNED;
   if (k_scale && (!aligned4(k_scale) || !aligned4(v_scale))) return ATTN_ERR_MISALIGNED;
-  const int S = splits_for(B, Hkv, group, max_blocks_per_seq, num_splits);
+  int S = splits_for(B, Hkv, group, max_blocks_per_seq, num_splits);
+  // The fp8 kernel runs four waves per (split, head, sequence), merged in LDS
+  // (it holds three waves per SIMD, so a workgroup of four does not hold a CU
+  // idle behind its slowest wave): a quarter of the automatic split count gives
+  // its waves the same length with a quarter of the partials (64 sequences x
+  // 40 heads of 128 to 4096 keys: 2 splits of 4 waves take 247 us, 8 splits of
+  // one wave 255 us). The workspace size query stays that of the bf16 call,
+  // which is never smaller.
+  if (k_scale != nullptr && num_splits == 0) S = (S + 3) / 4;
   const size_t need = workspace_for(B, Hq, q_len, D, S);
   float* o_part = nullptr;
   float* lse_part = nullptr;

@@ -41,9 +41,10 @@ namespace attn {
 constexpr int kIdChunk = 256;  // block ids staged in LDS at a time (even)
 constexpr float kMaxPairSum = 1073741824.f;  // 2^30: bound on one lane's P sum per block pair
 
-// WPS waves per workgroup share one (split, head, sequence): wave w takes the
-// w-th part of the split's blocks and the parts are merged in LDS at the end,
-// which gives short-split launches more waves without more partials.
+// WPS waves per workgroup (1, 2 or 4) share one (split, head, sequence): wave
+// w takes the w-th part of the split's blocks and the parts are merged in LDS
+// at the end, which gives short-split launches more waves without more
+// partials.
 // Two E4M3 codes (the low or high half of a word) to two bf16, exactly.
 __device__ __forceinline__ uint32_t fp8x2_lo(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
@@ -411,29 +412,40 @@ void paged_attn_kernel(
 
   if constexpr (WPS > 1) {
     // merge the waves' states lane by lane (equal lanes hold the same query,
-    // output columns and key positions) into wave 0, through LDS
-    static_assert(WPS == 2, "two waves per split");
-    __syncthreads();  // both waves are done with their LDS staging areas
-    float* xch = (float*)vlds_raw[1];  // (2 + 4 DB) floats per lane
-    if (wave == 1) {
-      xch[lane] = m_run;
-      xch[64 + lane] = l_run;
+    // output columns and key positions) into wave 0, through LDS: waves 1 ..
+    // WPS-1 leave (m, l, O) in their own staging areas
+    static_assert(WPS == 2 || WPS == 4, "two or four waves per split");
+    __syncthreads();  // every wave is done with its LDS staging area
+    if (wave != 0) {
+      float* xw = (float*)vlds_raw[wave];  // (2 + 4 DB) floats per lane
+      xw[lane] = m_run;
+      xw[64 + lane] = l_run;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xch[128 + (db * 4 + j) * 64 + lane] = acc[db][j];
+        for (int j = 0; j < 4; ++j) xw[128 + (db * 4 + j) * 64 + lane] = acc[db][j];
     }
     __syncthreads();
-    if (wave == 1) return;
-    const float m1 = xch[lane];
-    const float m_new = fmaxf(m_run, m1);
-    const float a0 = m_run == m_new ? 1.f : exp2_fast((m_run - m_new) * cs);  // 0 when m_run = -inf
-    const float a1 = m1 == m_new ? 1.f : exp2_fast((m1 - m_new) * cs);
-    l_run = a0 * l_run + a1 * xch[64 + lane];
+    if (wave != 0) return;
+    float m_new = m_run;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int w = 1; w < WPS; ++w) m_new = fmaxf(m_new, ((const float*)vlds_raw[w])[lane]);
+    // an unchanged m (also -inf == -inf) keeps weight 1; an unset m gives 0
+    const float a0 = m_run == m_new ? 1.f : exp2_fast((m_run - m_new) * cs);
+    l_run *= a0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[db][j] = a0 * acc[db][j] + a1 * xch[128 + (db * 4 + j) * 64 + lane];
+    for (int db = 0; db < DB; ++db) acc[db] *= a0;
+#pragma unroll
+    for (int w = 1; w < WPS; ++w) {
+      const float* xw = (const float*)vlds_raw[w];
+      const float mw = xw[lane];
+      const float aw = mw == m_new ? 1.f : exp2_fast((mw - m_new) * cs);
+      l_run += aw * xw[64 + lane];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[db][j] += aw * xw[128 + (db * 4 + j) * 64 + lane];
+    }
     m_run = m_new;
   }
 
@@ -559,13 +571,15 @@ static void launch_paged_variant(dim3 grid, hipStream_t stream, const PagedArgs&
 }
 
 template <bool F8>
-static void launch_paged_dispatch(int D, bool two, dim3 grid, hipStream_t stream,
+static void launch_paged_dispatch(int D, int wps, dim3 grid, hipStream_t stream,
                                   const PagedArgs& a) {
   if (D == 128) {
-    if (two) launch_paged_variant<128, 2, F8>(grid, stream, a);
+    if (wps == 4) launch_paged_variant<128, 4, F8>(grid, stream, a);
+    else if (wps == 2) launch_paged_variant<128, 2, F8>(grid, stream, a);
     else launch_paged_variant<128, 1, F8>(grid, stream, a);
   } else {
-    if (two) launch_paged_variant<64, 2, F8>(grid, stream, a);
+    if (wps == 4) launch_paged_variant<64, 4, F8>(grid, stream, a);
+    else if (wps == 2) launch_paged_variant<64, 2, F8>(grid, stream, a);
     else launch_paged_variant<64, 1, F8>(grid, stream, a);
   }
 }
@@ -580,12 +594,14 @@ hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_po
                              float scale, hipStream_t stream) {
   dim3 grid(num_splits, H, B);
   // With few (split, head, sequence) items the resident waves would leave part
-  // of the chip idle in the last round; give each item two waves instead.
-  const bool two = (long long)num_splits * H * B < 4096;
+  // of the chip idle in the last round; give each item two waves instead. The
+  // fp8 variant always runs four waves per item (its host side takes a
+  // quarter of the splits).
+  const int wps = k_scale != nullptr ? 4 : (long long)num_splits * H * B < 4096 ? 2 : 1;
   const PagedArgs a{q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, o, lse, o_part,
                     lse_part, H, group, q_len, max_blocks, num_splits, causal, scale};
-  if (k_scale != nullptr) launch_paged_dispatch<true>(D, two, grid, stream, a);
-  else launch_paged_dispatch<false>(D, two, grid, stream, a);
+  if (k_scale != nullptr) launch_paged_dispatch<true>(D, wps, grid, stream, a);
+  else launch_paged_dispatch<false>(D, wps, grid, stream, a);
   return hipGetLastError();
 }
 
