@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __attribute__((aligned(1024))) unsigned char ks1[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char vs0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char vs1[C::TILEB];
-  __shared__ int ids[PAGED ? kPagedMaxBlocks : 1];
+  __shared__ __attribute__((aligned(16))) int ids[PAGED ? kPagedMaxBlocks : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,15 +213,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if constexpr (decltype(s)::value == 0) return (ATTN_LDS unsigned char*)vs0;
     else return (ATTN_LDS unsigned char*)vs1;
   };
-  // paged: the buffer range of piece i of tile kt -- the piece's rows inside
-  // their cache block, ending at the sequence's last key (rows past it, and
-  // pieces wholly past it, read as zeros)
-  auto paged_piece = [&](const bf16* pool, int kt, int i) -> __amdgpu_buffer_rsrc_t {
-    const int key = kt * BN + (wave + NW * i) * C::RPP;
-    if (key >= Lk) return buffer_rsrc(pool, 0);
-    const int blk = __builtin_amdgcn_readfirstlane(ids[key >> 4]);
-    const bf16* src = pool + (((size_t)blk * pg.kv_heads + kvh) * 16 + (key & 15)) * D;
-    return buffer_rsrc(src, min(C::RPP, Lk - key) * C::ROWB);
+  // paged: a key tile (BN = 64 keys) spans exactly four cache blocks, ids
+  // 4 kt .. 4 kt + 3, read with one 16-byte LDS load (index at most 2047, since
+  // Lk <= 16 kPagedMaxBlocks; entries past the sequence's blocks are never
+  // used). One load and one wait per tile instead of one per 1 KiB piece.
+  static_assert(!PAGED || BN == 64, "a paged key tile spans four cache blocks");
+  auto tile_blocks = [&](int kt) -> i32x4 { return *reinterpret_cast<const i32x4*>(ids + 4 * kt); };
+  // the buffer range of piece i of tile kt -- the piece's rows inside their
+  // cache block, ending at the sequence's last key (rows past it, and pieces
+  // wholly past it, read as zeros). The block is chosen among the tile's four
+  // by value selects (no indexed access, which would go through scratch).
+  auto paged_piece = [&](const bf16* pool, int kt, int i, i32x4 bl) -> __amdgpu_buffer_rsrc_t {
+    const int off_in_tile = (wave + NW * i) * C::RPP;
+    const int key = kt * BN + off_in_tile;
+    const int which = off_in_tile >> 4;  // 0 .. 3, wave-uniform
+    const int lo = (which & 1) ? bl[1] : bl[0];
+    const int hi = (which & 1) ? bl[3] : bl[2];
+    const int id = __builtin_amdgcn_readfirstlane((which & 2) ? hi : lo);
+    const bool live = key < Lk;
+    const bf16* src = pool + (((size_t)(live ? id : 0) * pg.kv_heads + kvh) * 16 + (key & 15)) * D;
+    return buffer_rsrc(src, live ? min(C::RPP, Lk - key) * C::ROWB : 0);
   };
   // Dense source of piece i of tile kt: rows kt * BN + NW * RPP * i onwards,
   // bounded by the head's L rows so that the ragged tail reads zeros.
@@ -231,8 +242,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   auto issue_k = [&](auto s, int kt) {
     if constexpr (PAGED) {
+      const i32x4 bl = tile_blocks(kt);
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i), kst(s) + (wave + NW * i) * 1024, koff);
+      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i, bl), kst(s) + (wave + NW * i) * 1024, koff);
     } else {
 #pragma unroll
       for (int i = 0; i < C::PPW; ++i) dma16(dense_piece(kh, kt, i), kst(s) + (wave + NW * i) * 1024, koff);
@@ -240,8 +252,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   auto issue_v = [&](auto s, int kt) {
     if constexpr (PAGED) {
+      const i32x4 bl = tile_blocks(kt);
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i), vst(s) + (wave + NW * i) * 1024, voff);
+      for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i, bl), vst(s) + (wave + NW * i) * 1024, voff);
     } else {
 #pragma unroll
       for (int i = 0; i < C::PPW; ++i) dma16(dense_piece(vh, kt, i), vst(s) + (wave + NW * i) * 1024, voff);
