@@ -77,7 +77,7 @@ void paged_attn_kernel(
   const KV* k_pool = static_cast<const KV*>(k_pool_);
   const KV* v_pool = static_cast<const KV*>(v_pool_);
   __shared__ __attribute__((aligned(16))) unsigned char vlds_raw[WPS][2 * 16 * PV];
-  __shared__ int ids_raw[WPS][kIdChunk];
+  __shared__ __attribute__((aligned(16))) int ids_raw[WPS][kIdChunk];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   ATTN_LDS unsigned char* vlds = (ATTN_LDS unsigned char*)vlds_raw[wave];
   ATTN_LDS int* ids = (ATTN_LDS int*)ids_raw[wave];
@@ -173,10 +173,14 @@ void paged_attn_kernel(
   // the block ids of the current chunk [c0, c1) of this split sit in LDS;
   // an id is read with a wave-uniform LDS load (no wait on global loads)
   int c0 = blk0, c1 = blk0;
-  auto block_id = [&](int n) -> int { return __builtin_amdgcn_readfirstlane(ids[n - c0]); };
+  // Both ids of the pair come from one 8-byte LDS read: pairs start at even
+  // offsets of the chunk, and when a pair has no second block the chunk has an
+  // odd length (kIdChunk is even), so the second entry is still inside ids.
   auto load = [&](int n, Pair& r) {
     const bool has_b = n + 1 < c1;
-    const int pa = block_id(n);
+    const i32x2 pair_ids = *reinterpret_cast<const ATTN_LDS i32x2*>(ids + (n - c0));
+    const int pa = __builtin_amdgcn_readfirstlane(pair_ids[0]);
+    const int pb_any = __builtin_amdgcn_readfirstlane(pair_ids[1]);
     if constexpr (F8) {
       const uint8_t* ka_src = k_pool + (size_t)pa * blk_stride + head_off;
       const uint8_t* va_src = v_pool + (size_t)pa * blk_stride + head_off;
@@ -188,7 +192,7 @@ void paged_attn_kernel(
       r.ska = k_scale[(size_t)pa * H + h];
       r.sva = v_scale[(size_t)pa * H + h];
       if (has_b) {
-        const int pb = block_id(n + 1);
+        const int pb = pb_any;
         const uint8_t* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
         const uint8_t* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
 #pragma unroll
@@ -215,7 +219,7 @@ void paged_attn_kernel(
 #pragma unroll
     for (int i = 0; i < VCH; ++i) r.va[i] = load_stream(va_src + (i * 64 + lane) * 8);
     if (has_b) {
-      const int pb = block_id(n + 1);
+      const int pb = pb_any;
       const bf16* kb_src = k_pool + (size_t)pb * blk_stride + head_off;
       const bf16* vb_src = v_pool + (size_t)pb * blk_stride + head_off;
 #pragma unroll
