@@ -48,7 +48,7 @@ def _cmp(o, lse, ro, rl, tol):
     return e, el
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(32))
 def test_prefill_random_shapes(api, case):
     rnd = random.Random(1000 + case)
     dtype = "f32" if case % 4 == 3 else "bf16"
@@ -71,7 +71,7 @@ def test_prefill_random_shapes(api, case):
     assert el <= (1e-5 if dtype == "f32" else TOL_LSE)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(32))
 def test_paged_decode_random_shapes(api, case):
     rnd = random.Random(2000 + case)
     D = rnd.choice([64, 128])
@@ -100,7 +100,7 @@ def test_paged_decode_random_shapes(api, case):
     assert e <= TOL_BF16 and el <= TOL_LSE
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_paged_prefill_varlen_random(api, case):
     rnd = random.Random(4000 + case)
     D = rnd.choice([64, 128])
@@ -137,7 +137,7 @@ def test_paged_prefill_varlen_random(api, case):
     assert e <= TOL_BF16 and el <= TOL_LSE
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(20))
 def test_fp8_decode_random_shapes(api, case):
     rnd = random.Random(7000 + case)
     D = rnd.choice([64, 128])
