@@ -320,11 +320,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bool need_mask = CAUSAL ? (key0 + BN - 1 > off + wrow0) : (key0 + BN > Lk);
     if (need_mask) {
       const int lim = (CAUSAL ? off + my_row : Lk - 1) - key0 - 4 * g;
+      // last key that the wave's first / last row sees (wave-uniform): a
+      // 32-key block wholly below the first is left alone, one wholly above the
+      // last is cleared, only a block in between is masked key by key
+      const int lo = CAUSAL ? off + wrow0 : Lk - 1;
+      const int hi = CAUSAL ? off + wrow0 + 31 : Lk - 1;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        const int kfirst = key0 + 32 * kb;
+        if (kfirst + 31 <= lo) continue;
+        if (kfirst > hi) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sc[kb][j] = -INFINITY;
+          continue;
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           sc[kb][j] = (kb * 32 + 8 * (j >> 2) + (j & 3) <= lim) ? sc[kb][j] : -INFINITY;
+      }
     }
   };
   // P = 2^(c s - mc) as the bf16 B operands of O^T += V^T P^T; returns this
@@ -399,6 +412,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   wait_vmcnt<0>();
   lds_barrier();
   qk(sa, kst(std::integral_constant<int, 0>{}));
+  // the reference of every row is set from its first tile here, before the
+  // pipelined loop, so that tile takes the common path (one pass of
+  // exponentials, no rescale of the still-zero l and O)
+  mask(sa, 0);
+  (void)move_max(sa);
 
   // Iteration j (every wave takes part in its barrier and loads): tile j's
   // scores are in s_cur, K_{j+1} and V_j are in LDS. The loop is split by
