@@ -468,22 +468,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   const float l_tot = sum_xor32(l_run);
-  if (my_row < L) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = o + qo_off + my_row * row_stride;
+  // O goes through the K stages, idle once every wave has passed the barrier
+  // below: written in the accumulator layout with each row's 16-byte chunks
+  // XOR-swizzled (conflict-free both ways), read back row-major, and stored 16
+  // bytes per lane so that 8 lanes write a whole 128-byte line, with the
+  // streaming (nontemporal) policy: the lines leave the L2 during the launch
+  // instead of in the write-back at its end.
+  lds_barrier();
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int wbyte = wave * 32 * C::ROWB;
+  ATTN_LDS unsigned char* ob = wbyte < C::TILEB ? kst(std::integral_constant<int, 0>{}) + wbyte
+                                                : kst(std::integral_constant<int, 1>{}) + (wbyte - C::TILEB);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = db * 32 + 8 * jj + 4 * g;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
-        w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d) = w;
-      }
-    if (lse != nullptr && g == 0)
-      lse[lse_off + my_row * lse_stride] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = db * 4 + jj;
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * jj + 0] * inv, acc[db][4 * jj + 1] * inv);
+      w[1] = pack_bf16x2(acc[db][4 * jj + 2] * inv, acc[db][4 * jj + 3] * inv);
+      *reinterpret_cast<ATTN_LDS u32x2*>(ob + l32 * C::ROWB + ((c ^ (l32 & (C::NCH - 1))) * 16) + 8 * g) = w;
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  constexpr int RPI = 64 / C::NCH;      // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / C::NCH;
+    const int c = lane % C::NCH;
+    const u32x4 w = *reinterpret_cast<const ATTN_LDS u32x4*>(ob + r * C::ROWB + ((c ^ (r & (C::NCH - 1))) * 16));
+    const int grow = wrow0 + r;
+    if (grow < L) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o + qo_off + grow * row_stride + c * 8));
   }
+  if (my_row < L && lse != nullptr && g == 0)
+    lse[lse_off + my_row * lse_stride] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
 }
 
 template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
