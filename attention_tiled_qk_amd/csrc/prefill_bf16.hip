@@ -234,12 +234,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const bf16* src = pool + (((size_t)(live ? id : 0) * pg.kv_heads + kvh) * 16 + (key & 15)) * D;
     return buffer_rsrc(src, live ? min(C::RPP, Lk - key) * C::ROWB : 0);
   };
-  // Dense source of piece i of tile kt: rows kt * BN + NW * RPP * i onwards,
-  // bounded by the head's L rows so that the ragged tail reads zeros.
-  auto dense_piece = [&](const bf16* head, int kt, int i) -> __amdgpu_buffer_rsrc_t {
-    const int row0 = kt * BN + NW * C::RPP * i;
-    return buffer_rsrc(head + (size_t)row0 * D, max(L - row0, 0) * C::ROWB);
-  };
+  // Dense source: one buffer range per head, its L rows of K or V. The tile and
+  // piece offsets ride in the per-lane offset (soffset stays 0), which the
+  // range check covers, so rows past L read as zeros; per piece the issue is one
+  // vector add instead of a descriptor built on the scalar unit.
+  const __amdgpu_buffer_rsrc_t k_head = buffer_rsrc(kh, PAGED ? 0 : L * C::ROWB);
+  const __amdgpu_buffer_rsrc_t v_head = buffer_rsrc(vh, PAGED ? 0 : L * C::ROWB);
   auto issue_k = [&](auto s, int kt) {
     if constexpr (PAGED) {
       const i32x4 bl = tile_blocks(kt);
@@ -247,7 +247,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i, bl), kst(s) + (wave + NW * i) * 1024, koff);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(dense_piece(kh, kt, i), kst(s) + (wave + NW * i) * 1024, koff);
+      for (int i = 0; i < C::PPW; ++i)
+        dma16(k_head, kst(s) + (wave + NW * i) * 1024, koff + (unsigned)((kt * BN + NW * C::RPP * i) * C::ROWB));
     }
   };
   auto issue_v = [&](auto s, int kt) {
@@ -257,7 +258,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i, bl), vst(s) + (wave + NW * i) * 1024, voff);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(dense_piece(vh, kt, i), vst(s) + (wave + NW * i) * 1024, voff);
+      for (int i = 0; i < C::PPW; ++i)
+        dma16(v_head, vst(s) + (wave + NW * i) * 1024, voff + (unsigned)((kt * BN + NW * C::RPP * i) * C::ROWB));
     }
   };
 
