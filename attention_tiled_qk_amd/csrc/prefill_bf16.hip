@@ -11,8 +11,9 @@
 //   * K/V tiles move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
 //     register round trip). K and V have two LDS stages each: while K_{j+1} and
 //     V_j are read, K_{j+2} and V_{j+1} are in flight; one barrier per tile.
-//     The buffer descriptor of each tile ends at the head's last key, so rows
-//     past L arrive as zeros.
+//     The buffer range ends at the head's last key (dense: one range per head,
+//     tile offsets in the per-lane offset; paged: one per cache-block piece),
+//     so rows past L arrive as zeros.
 //   * LDS tiles are unpadded; 16-byte chunks are XOR-swizzled per row (a
 //     different swizzle for K and for V) so that the K operand reads and the
 //     transposing V reads below are free of bank conflicts. The swizzle is
@@ -28,14 +29,17 @@
 //     the same basic block as the exponentials of tile j, so one wave's matrix
 //     cores and vector ALUs work at the same time;
 //   * reference max: any reference m gives the same O = sum(e^(s-m) v) /
-//     sum(e^(s-m)). The exponentials use the current m; only when a lane's P
-//     sum over a tile reaches 2^30 (or m is unset) is the row max taken, m
-//     moved, l and O rescaled and P recomputed -- rare after the first tile;
+//     sum(e^(s-m)). m is set from each row's first tile before the loop; the
+//     exponentials use the current m, and only when a lane's P sum over a tile
+//     reaches 2^30 is the row max taken, m moved, l and O rescaled and P
+//     recomputed -- rare;
 //   * causal: key tiles above a wave's last row are skipped, the mask is only
 //     evaluated on tiles that cross the diagonal, and the work order (tile_of)
 //     keeps each head on one XCD and starts the longest query tiles first;
 //     launches with evenly loaded tiles (full attention, paged chunks) run a
-//     head's query tiles side by side instead (tile_of_head_major).
+//     head's query tiles side by side instead (tile_of_head_major);
+//   * epilogue: O leaves through LDS (the idle K stages) as whole 128-byte
+//     lines with streaming stores, so it drains during the launch.
 #include <type_traits>
 
 #include "common.h"
