@@ -15,7 +15,7 @@ hipError_t launch_prefill_bf16(const void*, const void*, const void*, void*, flo
                                int, int, float, hipStream_t);
 hipError_t launch_paged_prefill_bf16(const void*, const void*, const void*, const int32_t*,
                                      const int32_t*, void*, float*, int, int, int, int, int, int,
-                                     float, hipStream_t, const int32_t*, int);
+                                     float, hipStream_t, const int32_t*, int, int);
 int paged_prefill_max_blocks();
 hipError_t launch_prefill_f32(const void*, const void*, const void*, void*, float*, int, int, int,
                               int, int, float, hipStream_t);
@@ -245,7 +245,7 @@ int attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
                                                     lse, B, H, q_len, D, max_blocks_per_seq,
                                                     causal, scale,
                                                     reinterpret_cast<hipStream_t>(stream), nullptr,
-                                                    H));
+                                                    H, num_blocks));
 }
 
 int attn_paged_prefill_varlen(const void* q, const void* k_pool, const void* v_pool,
@@ -293,7 +293,7 @@ int attn_paged_prefill_gqa(const void* q, const void* k_pool, const void* v_pool
                                                     lse, B, H, max_q_len, D, max_blocks_per_seq,
                                                     causal, scale,
                                                     reinterpret_cast<hipStream_t>(stream),
-                                                    cu_q_lens, Hkv));
+                                                    cu_q_lens, Hkv, num_blocks));
 }
 
 size_t attn_paged_gqa_workspace_bytes(int B, int Hq, int Hkv, int q_len, int D,

@@ -129,9 +129,10 @@ struct PagedKV {
   int heads;                    // query heads per sequence
   int max_blocks;
   int kv_heads;                 // heads of the pools; query head h reads h / (heads / kv_heads)
+  int pool_bytes;               // bytes of each pool when below 2^31 (one buffer range each), else 0
 };
 
-template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
+template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false, bool POOL = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_bf16_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int L, int n_heads, int n_qtiles, float scale,
@@ -244,8 +245,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // vector add instead of a descriptor built on the scalar unit.
   const __amdgpu_buffer_rsrc_t k_head = buffer_rsrc(kh, PAGED ? 0 : L * C::ROWB);
   const __amdgpu_buffer_rsrc_t v_head = buffer_rsrc(vh, PAGED ? 0 : L * C::ROWB);
+  // Paged, pools below 2 GiB: one buffer range per pool. A piece's cache-block
+  // offset (a few scalar instructions) and the lane's row in the piece ride in
+  // the per-lane offset; lanes whose key is past the sequence's end take an
+  // offset beyond the range and read zeros.
+  const __amdgpu_buffer_rsrc_t k_pool_rs = buffer_rsrc(k, POOL ? pg.pool_bytes : 0);
+  const __amdgpu_buffer_rsrc_t v_pool_rs = buffer_rsrc(v, POOL ? pg.pool_bytes : 0);
+  const int lane_row = lane / C::NCH;
+  auto pool_off = [&](int kt, int i, i32x4 bl, unsigned lane_off) -> unsigned {
+    const int off_in_tile = (wave + NW * i) * C::RPP;
+    const int key = kt * BN + off_in_tile;
+    const int which = off_in_tile >> 4;  // 0 .. 3, wave-uniform
+    const int lo = (which & 1) ? bl[1] : bl[0];
+    const int hi = (which & 1) ? bl[3] : bl[2];
+    const unsigned id = (unsigned)__builtin_amdgcn_readfirstlane((which & 2) ? hi : lo);
+    const unsigned base = ((id * (unsigned)pg.kv_heads + (unsigned)kvh) * 16u + (unsigned)(key & 15)) * (unsigned)C::ROWB;
+    return lane_row < Lk - key ? base + lane_off : 0x80000000u;
+  };
   auto issue_k = [&](auto s, int kt) {
-    if constexpr (PAGED) {
+    if constexpr (PAGED && POOL) {
+      const i32x4 bl = tile_blocks(kt);
+#pragma unroll
+      for (int i = 0; i < C::PPW; ++i) dma16(k_pool_rs, kst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, koff));
+    } else if constexpr (PAGED) {
       const i32x4 bl = tile_blocks(kt);
 #pragma unroll
       for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(k, kt, i, bl), kst(s) + (wave + NW * i) * 1024, koff);
@@ -256,7 +278,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
   auto issue_v = [&](auto s, int kt) {
-    if constexpr (PAGED) {
+    if constexpr (PAGED && POOL) {
+      const i32x4 bl = tile_blocks(kt);
+#pragma unroll
+      for (int i = 0; i < C::PPW; ++i) dma16(v_pool_rs, vst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, voff));
+    } else if constexpr (PAGED) {
       const i32x4 bl = tile_blocks(kt);
 #pragma unroll
       for (int i = 0; i < C::PPW; ++i) dma16(paged_piece(v, kt, i, bl), vst(s) + (wave + NW * i) * 1024, voff);
@@ -509,15 +535,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     lse[lse_off + my_row * lse_stride] = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
 }
 
-template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false>
+template <int D, int NW, int BN, bool CAUSAL, bool PAGED = false, bool POOL = false>
 hipError_t launch_prefill_pipe(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int L, float scale, hipStream_t stream,
-                               PagedKV pg = PagedKV{nullptr, nullptr, nullptr, 0, 0, 0}) {
+                               PagedKV pg = PagedKV{nullptr, nullptr, nullptr, 0, 0, 0, 0}) {
   using C = PrefillCfg<D, NW, BN>;
   const int n_qtiles = (L + C::BM - 1) / C::BM;
   const long long grid = (long long)B * H * n_qtiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_pipe_kernel<D, NW, BN, CAUSAL, PAGED>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_bf16_pipe_kernel<D, NW, BN, CAUSAL, PAGED, POOL>), dim3((unsigned)grid),
                      dim3(C::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                      (bf16*)o, lse, L, B * H, n_qtiles, scale, pg);
   return hipGetLastError();
@@ -544,20 +570,29 @@ hipError_t launch_paged_prefill_bf16(const void* q, const void* k_pool, const vo
                                      const int32_t* block_tables, const int32_t* seq_lens, void* o,
                                      float* lse, int B, int H, int q_len, int D, int max_blocks,
                                      int causal, float scale, hipStream_t stream,
-                                     const int32_t* cu_q, int Hkv) {
+                                     const int32_t* cu_q, int Hkv, int num_blocks) {
   // with cu_q, q_len is the longest sequence's query count (it sizes the grid);
   // H query heads read the pools' Hkv heads in groups of H / Hkv
-  const PagedKV pg{block_tables, seq_lens, cu_q, H, max_blocks, Hkv};
+  const long long pool_bytes = (long long)num_blocks * Hkv * 16 * D * 2;
+  const bool pool32 = pool_bytes < 0x80000000LL;
+  const PagedKV pg{block_tables, seq_lens, cu_q, H, max_blocks, Hkv, pool32 ? (int)pool_bytes : 0};
+  auto go = [&](auto d, auto c, auto p) {
+    constexpr int DD = decltype(d)::value;
+    constexpr bool CC = decltype(c)::value;
+    constexpr bool PP = decltype(p)::value;
+    return launch_prefill_pipe<DD, 4, 64, CC, true, PP>(q, k_pool, v_pool, o, lse, B, H, q_len, scale,
+                                                        stream, pg);
+  };
+  using D128 = std::integral_constant<int, 128>;
+  using D64 = std::integral_constant<int, 64>;
+  using T = std::true_type;
+  using F = std::false_type;
   if (D == 128) {
-    return causal ? launch_prefill_pipe<128, 4, 64, true, true>(q, k_pool, v_pool, o, lse, B, H,
-                                                                q_len, scale, stream, pg)
-                  : launch_prefill_pipe<128, 4, 64, false, true>(q, k_pool, v_pool, o, lse, B, H,
-                                                                 q_len, scale, stream, pg);
+    if (causal) return pool32 ? go(D128{}, T{}, T{}) : go(D128{}, T{}, F{});
+    return pool32 ? go(D128{}, F{}, T{}) : go(D128{}, F{}, F{});
   }
-  return causal ? launch_prefill_pipe<64, 4, 64, true, true>(q, k_pool, v_pool, o, lse, B, H, q_len,
-                                                             scale, stream, pg)
-                : launch_prefill_pipe<64, 4, 64, false, true>(q, k_pool, v_pool, o, lse, B, H, q_len,
-                                                              scale, stream, pg);
+  if (causal) return pool32 ? go(D64{}, T{}, T{}) : go(D64{}, T{}, F{});
+  return pool32 ? go(D64{}, F{}, T{}) : go(D64{}, F{}, F{});
 }
 
 }  // namespace attn

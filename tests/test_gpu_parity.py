@@ -363,6 +363,56 @@ def test_paged_prefill_bit_identical_under_block_permutation(api):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_paged_prefill_pool_over_2gib_matches_compact_pool(api):
+    """Pools of 2^31 bytes or more take the kernel's other addressing path (a
+    buffer range per 1 KiB piece instead of one per pool). The same problem laid
+    out in a 2.15 GB pool -- blocks near its end, every other slot NaN -- and in
+    a compact pool must give bit-identical outputs and log-sum-exps."""
+    H, D, nb_big = 8, 128, 65600          # 65600 * 8 * 16 * 128 * 2 bytes > 2^31
+    lens = (300, 1000)
+    q_len = 64
+    need = [(n + 15) // 16 for n in lens]
+    g = torch.Generator().manual_seed(91)
+    total = sum(need)
+    k_small = torch.randn(total, H, 16, D, generator=g).to(torch.bfloat16)
+    v_small = torch.randn(total, H, 16, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(len(lens), H, q_len, D, generator=g).to(torch.bfloat16)
+    width = max(need)
+    tab_small = torch.full((len(lens), width), -1, dtype=torch.int32)
+    tab_big = torch.full((len(lens), width), -1, dtype=torch.int32)
+    # big-pool ids: the last blocks of the pool for the first sequence, a spread
+    # across the pool (ending near its top) for the second
+    big_ids = list(range(nb_big - need[0], nb_big)) + [100 + 1000 * i for i in range(need[1])]
+    c = 0
+    for b, n in enumerate(need):
+        for j in range(n):
+            tab_small[b, j] = c
+            tab_big[b, j] = big_ids[c]
+            c += 1
+    dev = torch.device("cuda")
+    k_big = torch.full((nb_big, H, 16, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    v_big = torch.full((nb_big, H, 16, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    idx = torch.tensor(big_ids, dtype=torch.long, device=dev)
+    k_sd, v_sd = k_small.to(dev), v_small.to(dev)
+    # tail slots past each sequence's end stay NaN in the big pool as well
+    for b, n in enumerate(lens):
+        last = sum(need[:b + 1]) - 1
+        if n % 16:
+            k_sd[last, :, n % 16:] = float("nan")
+            v_sd[last, :, n % 16:] = float("nan")
+    k_big[idx] = k_sd
+    v_big[idx] = v_sd
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    qd = q.to(dev)
+    o1, l1 = api.attn_paged_prefill(qd, k_sd, v_sd, tab_small.to(dev), seq, causal=True, return_lse=True)
+    o2, l2 = api.attn_paged_prefill(qd, k_big, v_big, tab_big.to(dev), seq, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    del k_big, v_big
+    torch.cuda.empty_cache()
+
+
 def test_paged_prefill_fresh_sequence_matches_prefill(api):
     """A chunk that is the whole sequence (q_len == seq_len) is ordinary causal
     prefill of the gathered K/V: same kernel arithmetic, same result bits."""
