@@ -363,12 +363,15 @@ def test_paged_prefill_bit_identical_under_block_permutation(api):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_paged_prefill_pool_over_2gib_matches_compact_pool(api):
-    """Pools of 2^31 bytes or more take the kernel's other addressing path (a
-    buffer range per 1 KiB piece instead of one per pool). The same problem laid
-    out in a 2.15 GB pool -- blocks near its end, every other slot NaN -- and in
-    a compact pool must give bit-identical outputs and log-sum-exps."""
-    H, D, nb_big = 8, 128, 65600          # 65600 * 8 * 16 * 128 * 2 bytes > 2^31
+@pytest.mark.parametrize("nb_big", [65535, 65600])
+def test_paged_prefill_large_pool_matches_compact_pool(api, nb_big):
+    """A pool of 65535 blocks of 8 heads x 16 x 128 is 32 KiB short of 2^31 bytes
+    (one buffer range for the whole pool, per-lane offsets up to its top); 65600
+    blocks pass 2^31 and take the kernel's other addressing path (a buffer range
+    per 1 KiB piece). The same problem laid out in such a pool -- blocks near its
+    end, every other slot NaN -- and in a compact pool must give bit-identical
+    outputs and log-sum-exps."""
+    H, D = 8, 128
     lens = (300, 1000)
     q_len = 64
     need = [(n + 15) // 16 for n in lens]
