@@ -191,8 +191,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // to the piece's first row (paged: a piece's RPP rows are consecutive slots of
   // one cache block, contiguous in the pool). Piece i of this wave starts
   // NW * RPP rows (4096 bytes) after piece i - 1 and both swizzles repeat every
-  // 16 rows, so one offset per lane serves every piece, each piece having a buffer
-  // descriptor of its own.
+  // 16 rows, so one offset per lane serves every piece: the piece's own position
+  // is added to it (dense, and paged pools below 2 GiB) or is the start of the
+  // piece's buffer range (larger pools).
   static_assert(NW * C::RPP * C::ROWB == 4096, "piece stride");
   unsigned koff, voff;
   {
