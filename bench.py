@@ -29,7 +29,11 @@ each with its own roofline entry (MFMA TFLOP/s or HBM GB/s); and
     patterns -- 4 KiB and 2 KiB blocks of a 2.5 GiB buffer in random order,
     and 4 KiB blocks in address order (attn_probe_block_read, loads only,
     nontemporal like the paged kernels; random 4 KiB also with the default
-    cache policy). The
+    cache policy).
+Each prefill and paged decode entry also carries ``cache_control``: the median
+single-launch time with warm caches and after a 512 MiB scratch write that
+evicts the MALL, so that the timed rate can be read against a cold-cache one.
+The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
 
@@ -113,6 +117,52 @@ def time_launches(torch, fn, warmup, steps):
     return start.elapsed_time(end) / steps, wall
 
 
+FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB last-level (MALL) cache
+
+
+def cache_control(torch, fn, calls=20):
+    """Single launches timed one by one with HIP events, with the caches warm
+    and cold. Each sample runs the same work -- one pass over a 512 MiB scratch
+    buffer and two launches -- and times the second launch: warm, the pass
+    comes first and the untimed launch re-reads the inputs into the caches;
+    cold, the pass sits between the two launches and evicts the L2s and the
+    MALL. The pass is a write (which also leaves dirty lines for the timed
+    launch to share HBM with while they drain) or a read (which leaves none).
+    The medians (us) bound the help the last-level cache gives the timed rate,
+    whose back-to-back launches may find part of their inputs still cached."""
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    words = scratch.view(torch.int32)
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+    passes = {"write": lambda i: scratch.fill_(i & 255),
+              "read": lambda i: torch.sum(words, dim=0, dtype=torch.int64, out=sink)}
+    res = {"flush_bytes": FLUSH_BYTES, "calls": calls}
+    fn()
+    torch.cuda.synchronize()
+    for kind, flush in passes.items():
+        res[kind] = {}
+        for name, between in (("warm_us", False), ("flushed_us", True)):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(calls)]
+            for i, (a, b) in enumerate(evs):
+                if not between:
+                    flush(i)
+                fn()
+                if between:
+                    flush(i)
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            res[kind][name] = times[calls // 2]
+    del scratch, words, sink
+    torch.cuda.empty_cache()
+    log("[bench]   cache control (single launches, medians): " + ", ".join(
+        f"{kind} pass {r['warm_us']:.1f} us warm / {r['flushed_us']:.1f} us flushed"
+        for kind, r in ((k, res[k]) for k in passes)))
+    return res
+
+
 def cpu_baseline(spec, budget_s):
     """Time the oracle on the host: one warm-up head, then up to three passes
     over the workload's (batch, head) pairs (each pass cut short at a third of
@@ -178,6 +228,7 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
             raise RuntimeError("attn_prefill failed")
 
     kernel_ms, wall = time_launches(torch, call, warmup, steps)
+    control = cache_control(torch, call)
     flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     traffic = load_traffic(key, source_digest(*KERNEL_SOURCES["prefill"]))
@@ -201,6 +252,7 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
             "algorithmic_flops_per_launch": flops,
             "launch_us_events": kernel_ms * 1e3,
         },
+        "cache_control": control,
     }
 
 
@@ -259,6 +311,7 @@ def bench_paged(torch, api, spec, warmup, steps, key):
             raise RuntimeError("paged decode failed")
 
     ms, wall = time_launches(torch, call, warmup, steps)
+    control = cache_control(torch, call)
     # K and V bytes of every visible token, as the sequences address them
     kv = 2.0 * H * D * 2 * sum(lens)
     # bytes that must come from HBM: the shared prefix blocks are read once
@@ -283,6 +336,7 @@ def bench_paged(torch, api, spec, warmup, steps, key):
             "logical_kv_bytes": kv,
             "launch_us_events": ms * 1e3,
         },
+        "cache_control": control,
     }
     del dq, dk, dv, dt, dl, ws, o
     torch.cuda.empty_cache()
@@ -311,6 +365,7 @@ def bench_paged_prefill(torch, api, spec, warmup, steps, key):
             raise RuntimeError("attn_paged_prefill failed")
 
     ms, wall = time_launches(torch, call, warmup, steps)
+    control = cache_control(torch, call)
     # visible (query, key) pairs: query t of a sequence of n keys sees n - q_len + t + 1
     pairs = 0
     for n in inp.seq_lens.tolist():
@@ -337,6 +392,7 @@ def bench_paged_prefill(torch, api, spec, warmup, steps, key):
             "algorithmic_flops_per_launch": flops,
             "launch_us_events": ms * 1e3,
         },
+        "cache_control": control,
     }
 
 
@@ -370,6 +426,7 @@ def bench_paged_fp8(torch, api, spec, warmup, steps, key):
             raise RuntimeError("attn_paged_decode_fp8 failed")
 
     ms, wall = time_launches(torch, call, warmup, steps)
+    control = cache_control(torch, call)
     # one byte per cached K and V value, plus the two scales of each (block, head)
     blocks = sum(-(-n // 16) for n in lens)
     kv = 2.0 * H * D * sum(lens) + 2.0 * 4 * H * blocks
@@ -393,6 +450,7 @@ def bench_paged_fp8(torch, api, spec, warmup, steps, key):
             "algorithmic_bytes_per_launch": kv,
             "launch_us_events": ms * 1e3,
         },
+        "cache_control": control,
     }
 
 
