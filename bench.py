@@ -163,6 +163,27 @@ def cache_control(torch, fn, calls=20):
     return res
 
 
+def device_info(torch):
+    """Compute units and peak engine clock of the current device, the peaks the
+    rooflines are priced against, and the dense bf16 matrix peak implied by
+    the units and clock (4096 FLOP per clock per CU)."""
+    import ctypes
+    dev = torch.cuda.current_device()
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "peak_bf16_tflops_used": PEAK_BF16_TFLOPS, "peak_hbm_gbs_used": PEAK_HBM_GBS}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        khz = ctypes.c_int(0)
+        HIP_ATTR_CLOCK_RATE_KHZ = 5  # hipDeviceAttributeClockRate
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), HIP_ATTR_CLOCK_RATE_KHZ, dev) == 0 and khz.value > 0:
+            info["max_engine_clock_mhz"] = khz.value / 1e3
+            info["peak_bf16_tflops_from_clock"] = p.multi_processor_count * 4096 * khz.value * 1e3 / 1e12
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(spec, budget_s):
     """Time the oracle on the host: one warm-up head, then up to three passes
     over the workload's (batch, head) pairs (each pass cut short at a third of
@@ -609,6 +630,7 @@ def main():
                    "B": C2.B, "H": C2.H, "L": C2.L, "D": C2.D, "causal": C2.causal,
                    "seed": C2.seed},
         "roofline": main_res["roofline"],
+        "device": device_info(torch),
         "secondary": {name: runners[name]() for name in ("c1", "c3", "c4", "c5", "c4g", "cpf", "append", "c4f8",
                                                          "probe")},
     }
