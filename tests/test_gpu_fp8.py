@@ -181,6 +181,47 @@ def test_decode_fp8(api, B, H, q_len, D, lens, qh, splits):
     assert e <= TOL_BF16 and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("splits", [0, 1])
+def test_decode_fp8_pool_past_2pow31_bytes_matches_compact_pool(api, splits):
+    """FP8 code pools of 131200 blocks of 8 heads x 16 x 128 hold more than 2^31
+    bytes each; blocks from 131072 on start past byte 2^31. The problem's blocks
+    moved to the end of such pools (every other block NaN codes and NaN
+    scales) give bit-identical outputs and log-sum-exps to the compact pools."""
+    spec = PagedSpec("fp8_big_pool", 3, 8, 1, 128, seed=77, len_lo=200, len_hi=1200, extra_blocks=3,
+                     poison=True)
+    inp = paged_inputs_fp8(spec)
+    nb_big = 131200
+    assert nb_big * 8 * 16 * 128 > 2**31 and 131072 * 8 * 16 * 128 == 2**31
+    n_small = inp.k_codes.shape[0]
+    off = nb_big - n_small
+    tab = inp.block_tables.clone()
+    tab[tab >= 0] += off
+    used = tab[tab >= 0]
+    assert int(used.max()) < nb_big and int((used >= 131072).sum()) > 0
+    dev = torch.device("cuda")
+    k_big = torch.full((nb_big, 8, BS, 128), 0x7F, dtype=torch.uint8, device=dev)
+    v_big = torch.full_like(k_big, 0x7F)
+    ks_big = torch.full((nb_big, 8), float("nan"), dtype=torch.float32, device=dev)
+    vs_big = torch.full_like(ks_big, float("nan"))
+    k_big[off:] = inp.k_codes.to(dev)
+    v_big[off:] = inp.v_codes.to(dev)
+    ks_big[off:] = inp.k_scale.to(dev)
+    vs_big[off:] = inp.v_scale.to(dev)
+    say(f"fp8 decode, pools of {nb_big} blocks, lens={inp.seq_lens.tolist()} S={splits}")
+    o1, l1 = _run(api, inp, splits)
+    o2, l2 = api.attn_paged_decode_fp8(inp.q.cuda(), k_big, v_big, ks_big, vs_big, tab.cuda(),
+                                       inp.seq_lens.cuda(), causal=True, scale=1.0 / math.sqrt(128),
+                                       num_splits=splits, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    e, el = _err(o2, l2, *_ref(inp))
+    say(f"  max|dO|={e:.3e} max|dlse|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_LSE
+    del k_big, v_big, ks_big, vs_big
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.05, 0.3])
 def test_decode_fp8_other_scales_and_full_attention(api, scale):
     spec = PagedSpec("fp8s", 3, 2, 3, 128, seed=61, len_lo=20, len_hi=400, poison=True)

@@ -368,12 +368,12 @@ def test_paged_prefill_bit_identical_under_block_permutation(api):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("nb_big", [65535, 65600])
+@pytest.mark.parametrize("nb_big", [65535, 65600, 131200])
 def test_paged_prefill_large_pool_matches_compact_pool(api, nb_big):
     """A pool of 65535 blocks of 8 heads x 16 x 128 is 32 KiB short of 2^31 bytes
     (one buffer range for the whole pool, per-lane offsets up to its top); 65600
-    blocks pass 2^31 and take the kernel's other addressing path (a buffer range
-    per 1 KiB piece). The same problem laid out in such a pool -- blocks near its
+    blocks pass 2^31 bytes and take the kernel's other addressing path (a buffer
+    range per 1 KiB piece); 131200 blocks pass 2^31 elements. The same problem laid out in such a pool -- blocks near its
     end, every other slot NaN -- and in a compact pool must give bit-identical
     outputs and log-sum-exps."""
     H, D = 8, 128
@@ -417,6 +417,97 @@ def test_paged_prefill_large_pool_matches_compact_pool(api, nb_big):
     torch.cuda.synchronize()
     assert torch.isfinite(o1.float()).all()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    del k_big, v_big
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_past_2pow31_elements(api, dtype):
+    """Q, K, V and O of B=1, H=16400, L=1024, D=128 hold 2^31 + 2^21 elements
+    each (4.3 GB in bf16, 8.6 GB in float32); head 16384 is the first to start
+    at element 2^31. The heads on both sides of that boundary, the first and
+    the last match the oracle: offsets are formed in 64 bits."""
+    B, H, L, D = 1, 16400, 1024, 128
+    assert B * H * L * D > 2**31 and 16384 * L * D == 2**31
+    dev = torch.device("cuda")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(93)
+    q, k, v = (torch.randn((B, H, L, D), device=dev, dtype=dt, generator=g) for _ in range(3))
+    scale = 1.0 / math.sqrt(D)
+    say(f"prefill {dtype} past 2^31 elements: B={B} H={H} L={L} D={D}")
+    o, lse = api.attn_prefill(q, k, v, causal=True, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    lse_tol = TOL_LSE if dtype == "bf16" else TOL_F32
+    for h in (0, 16383, 16384, H - 1):
+        ref_o, ref_lse = oracle.dense_attention(q[0, h].cpu(), k[0, h].cpu(), v[0, h].cpu(), scale, True)
+        e = float(np.abs(o[0, h].double().cpu().numpy() - ref_o).max())
+        el = float(np.abs(lse[0, h].double().cpu().numpy() - ref_lse).max())
+        say(f"  head {h}: max|dO|={e:.3e} max|dlse|={el:.3e}")
+        assert e <= tol and el <= lse_tol
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("q_len,splits", [(1, 0), (1, 1), (5, 16)])
+def test_paged_decode_pool_past_2pow31_elements_matches_compact_pool(api, q_len, splits):
+    """A pool of 131200 blocks of 8 heads x 16 x 128 holds more than 2^31
+    elements (4.3 GB each for K and V); blocks from 131072 on start past
+    element 2^31. The same problem laid out near the end of such a pool --
+    every other slot NaN -- and in a compact pool must give bit-identical
+    outputs and log-sum-exps."""
+    H, D, nb_big = 8, 128, 131200
+    assert nb_big * H * 16 * D > 2**31 and 131072 * H * 16 * D == 2**31
+    lens = (300, 1000)
+    need = [(n + 15) // 16 for n in lens]
+    g = torch.Generator().manual_seed(94)
+    total = sum(need)
+    k_small = torch.randn(total, H, 16, D, generator=g).to(torch.bfloat16)
+    v_small = torch.randn(total, H, 16, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(len(lens), H, q_len, D, generator=g).to(torch.bfloat16)
+    width = max(need)
+    tab_small = torch.full((len(lens), width), -1, dtype=torch.int32)
+    tab_big = torch.full((len(lens), width), -1, dtype=torch.int32)
+    # the first sequence in the pool's last blocks (all past element 2^31), the
+    # second spread across the pool, its last blocks past the boundary too
+    big_ids = (list(range(nb_big - need[0], nb_big)) + [2000 * i + 7 for i in range(need[1] - 4)]
+               + [131072 + 20 * j for j in range(4)])
+    assert max(big_ids) < nb_big and len(set(big_ids)) == len(big_ids)
+    assert sum(i >= 131072 for i in big_ids[need[0]:]) > 0
+    c = 0
+    for b, n in enumerate(need):
+        for j in range(n):
+            tab_small[b, j] = c
+            tab_big[b, j] = big_ids[c]
+            c += 1
+    dev = torch.device("cuda")
+    k_sd, v_sd = k_small.to(dev), v_small.to(dev)
+    for b, n in enumerate(lens):
+        last = sum(need[:b + 1]) - 1
+        if n % 16:
+            k_sd[last, :, n % 16:] = float("nan")
+            v_sd[last, :, n % 16:] = float("nan")
+    k_big = torch.full((nb_big, H, 16, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    v_big = torch.full((nb_big, H, 16, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    idx = torch.tensor(big_ids, dtype=torch.long, device=dev)
+    k_big[idx] = k_sd
+    v_big[idx] = v_sd
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    qd = q.to(dev)
+    say(f"paged decode, pool of {nb_big} blocks, q_len={q_len} splits={splits}")
+    o1, l1 = api.attn_paged_decode(qd, k_sd, v_sd, tab_small.to(dev), seq, causal=True,
+                                   num_splits=splits, return_lse=True)
+    o2, l2 = api.attn_paged_decode(qd, k_big, v_big, tab_big.to(dev), seq, causal=True,
+                                   num_splits=splits, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    scale = 1.0 / math.sqrt(D)
+    ref_o, ref_lse = oracle.paged_attention(q, k_sd.cpu(), v_sd.cpu(), tab_small, torch.tensor(lens),
+                                            scale, True)
+    e = max_err(o2, ref_o)
+    say(f"  max|dO|={e:.3e}")
+    assert e <= TOL_BF16 and lse_err(l2, ref_lse) <= TOL_LSE
     del k_big, v_big
     torch.cuda.empty_cache()
 
