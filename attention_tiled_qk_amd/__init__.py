@@ -22,7 +22,8 @@ __all__ = [
     "attn_paged_prefill_varlen", "attn_paged_prefill_gqa",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
     "KVCacheAllocator", "attn_paged_append_fp8", "attn_paged_copy_blocks_fp8",
-    "attn_paged_decode_fp8", "attn_probe_block_read", "attn_version", "lib", "LIB_PATH",
+    "attn_paged_decode_fp8", "attn_probe_block_read", "attn_paged_check_tables", "attn_version",
+    "lib", "LIB_PATH",
     "ATTN_F32", "ATTN_BF16",
 ]
 
@@ -66,6 +67,8 @@ lib.attn_lse_merge.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_lse_merge.restype = _i
 lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_gather.restype = _i
+lib.attn_paged_check_tables.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p]
+lib.attn_paged_check_tables.restype = _i
 lib.attn_probe_block_read.argtypes = [_p, _i, _i, _p, _i, _p, _i, _i, _p]
 lib.attn_probe_block_read.restype = _i
 lib.attn_paged_append.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
@@ -368,6 +371,22 @@ def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, st
                                nblk, width, max_seq_len, _stream(pool.device, stream))
     _check(st, "attn_paged_gather")
     return out
+
+
+def attn_paged_check_tables(block_tables, seq_lens, num_blocks, *, min_len=1, stream=None):
+    """Count, on the device, what the paged calls would read out of range:
+    returns (sequences whose length is below min_len or past the table's
+    16 * width keys, table entries those calls read whose id lies outside
+    [0, num_blocks)). Waits for the count (a debugging aid, not for hot loops)."""
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    B, width = block_tables.shape
+    bad = torch.empty(2, device=block_tables.device, dtype=torch.int32)
+    st = lib.attn_paged_check_tables(_ptr(block_tables), _ptr(seq_lens), B, min_len, num_blocks, width,
+                                     _ptr(bad), _stream(block_tables.device, stream))
+    _check(st, "attn_paged_check_tables")
+    n_len, n_id = bad.tolist()
+    return n_len, n_id
 
 
 def attn_probe_block_read(buf, block_bytes, order, n_waves, *, nontemporal=False, sink=None,

@@ -23,7 +23,7 @@ FLAGS = [
 ]
 SOURCES = [
     "attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "paged.hip", "kv_append.hip",
-    "kv_cache.hip", "probe.hip",
+    "kv_cache.hip", "probe.hip", "table_check.hip",
 ]
 
 

@@ -38,6 +38,8 @@ hipError_t launch_paged_copy_blocks_fp8(void*, void*, float*, float*, const int3
                                         const int32_t*, int, int, int, hipStream_t);
 hipError_t launch_probe_block_read(const void*, int, const int32_t*, int, uint32_t*, int, int,
                                    hipStream_t);
+hipError_t launch_check_tables(const int32_t*, const int32_t*, int, int, int, int, int32_t*,
+                               hipStream_t);
 }  // namespace attn
 
 namespace {
@@ -355,6 +357,18 @@ int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32
   if (!aligned4(block_tables) || !aligned4(seq_lens)) return ATTN_ERR_MISALIGNED;
   return hip_status(attn::launch_paged_gather(pool, block_tables, seq_lens, out, B, H, D,
                                               max_blocks_per_seq, max_seq_len,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_check_tables(const int32_t* block_tables, const int32_t* seq_lens, int B,
+                            int min_len, int num_blocks, int max_blocks_per_seq, int32_t* bad,
+                            void* stream) {
+  if (!block_tables || !seq_lens || !bad) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || min_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (checked_mul({B, max_blocks_per_seq}) < 0) return ATTN_ERR_OVERFLOW;
+  if (!aligned4(block_tables) || !aligned4(seq_lens) || !aligned4(bad)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_check_tables(block_tables, seq_lens, B, min_len, num_blocks,
+                                              max_blocks_per_seq, bad,
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 

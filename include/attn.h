@@ -36,7 +36,8 @@
  *   - Every argument is validated on the host before anything is enqueued. On
  *     error the call returns a negative ATTN_ERR_* code and enqueues nothing.
  *     Device-side contents are trusted: block ids outside [0, num_blocks) or
- *     seq_lens above max_blocks_per_seq * 16 are undefined behaviour.
+ *     seq_lens above max_blocks_per_seq * 16 are undefined behaviour;
+ *     attn_paged_check_tables counts such entries on the device.
  *   - Calls are stateless and re-entrant; calls on different streams may run
  *     concurrently if their output buffers do not overlap.
  */
@@ -290,6 +291,31 @@ int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* l
 int attn_paged_gather(const void* pool, const int32_t* block_tables, const int32_t* seq_lens,
                       void* out, int B, int H, int D, int num_blocks, int max_blocks_per_seq,
                       int max_seq_len, void* stream);
+
+/*
+ * attn_paged_check_tables -- count the entries of a paged-cache description
+ * that the attention, append and gather calls would read out of range. Those
+ * calls trust their tables ([P3] PagedAttention: a request's table lists the
+ * only blocks its kernel reads), so this is a debugging aid to run before
+ * them; it reads the tables only.
+ *
+ *   block_tables : [B, max_blocks_per_seq] int32 device.
+ *   seq_lens     : [B] int32 device.
+ *   min_len      : smallest valid length, >= 0 (the q_len of the call to check;
+ *                  0 for a ragged prefill).
+ *   bad          : 2 int32 device words, overwritten (not accumulated), each
+ *                  saturating at INT32_MAX:
+ *                  bad[0] = sequences with seq_lens[b] < min_len or
+ *                           > max_blocks_per_seq * 16;
+ *                  bad[1] = entries j < ceil(min(max(seq_lens[b], 0),
+ *                           max_blocks_per_seq * 16) / 16) of row b (the ones
+ *                           the calls read) outside [0, num_blocks).
+ * One workgroup, enqueued on stream; the counts are valid once it completes.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_check_tables(const int32_t* block_tables, const int32_t* seq_lens, int B,
+                            int min_len, int num_blocks, int max_blocks_per_seq, int32_t* bad,
+                            void* stream);
 
 /*
  * attn_paged_append -- write n_new new tokens of K and V per sequence into the

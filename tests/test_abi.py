@@ -187,6 +187,23 @@ def test_merge_and_gather_reject_bad_arguments(api):
     assert L.attn_paged_gather(FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 4, 4, 0, None) == c["ATTN_ERR_BAD_SHAPE"]
 
 
+def test_check_tables_rejects_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+
+    def call(tab=FAKE, lens=FAKE, B=2, min_len=1, nb=64, width=8, bad=FAKE):
+        return L.attn_paged_check_tables(tab, lens, B, min_len, nb, width, bad, None)
+
+    assert call(tab=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(lens=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(bad=None) == c["ATTN_ERR_NULL_PTR"]
+    assert call(B=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(min_len=-1) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(nb=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(width=0) == c["ATTN_ERR_BAD_SHAPE"]
+    assert call(bad=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
+
+
 def test_probe_rejects_bad_arguments(api):
     c = header_constants()
     L = api.lib

@@ -713,6 +713,51 @@ def test_gather_paging_figure(api):
 
 # -------------------------------------------------------------------- merge ---
 
+def _count_bad_entries(tables, lens, min_len, num_blocks):
+    """Host count, entry by entry, of what attn_paged_check_tables reports."""
+    width = len(tables[0])
+    bad_len = bad_id = 0
+    for row, n in zip(tables, lens):
+        if n < min_len or n > 16 * width:
+            bad_len += 1
+        for j in range((min(max(n, 0), 16 * width) + 15) // 16):
+            if not 0 <= row[j] < num_blocks:
+                bad_id += 1
+    return bad_len, bad_id
+
+
+def test_check_tables_counts_out_of_range_entries(api):
+    """The table check finds nothing wrong in a valid decode description, and
+    counts each planted fault: ids past the pool or negative inside a
+    sequence's range, lengths past the table or below q_len, a negative
+    length. Padding past a sequence's blocks is not counted."""
+    inp = paged_inputs(C4)
+    nb = inp.k_pool.shape[0]
+    tab = inp.block_tables.clone()
+    lens = inp.seq_lens.clone()
+    width = tab.shape[1]
+    dev = torch.device("cuda")
+    assert api.attn_paged_check_tables(tab.to(dev), lens.to(dev), nb) == (0, 0)
+    assert _count_bad_entries(tab.tolist(), lens.tolist(), 1, nb) == (0, 0)
+    tab[0, 0] = nb                              # one past the pool
+    tab[1, (int(lens[1]) - 1) // 16] = -1       # the last block of a sequence
+    tab[2, 3] = 1 << 30
+    n3 = int(lens[3])
+    tab[3, (n3 + 15) // 16:] = nb + 5           # padding: never read, not counted
+    n4 = int(lens[4])
+    lens[4] = 16 * width + 1                    # longer than the table: its -1 padding is read
+    lens[5] = 0                                 # shorter than q_len = 1
+    lens[6] = -7
+    expect = _count_bad_entries(tab.tolist(), lens.tolist(), 1, nb)
+    assert expect == (3, 3 + width - (n4 + 15) // 16)
+    got = api.attn_paged_check_tables(tab.to(dev), lens.to(dev), nb)
+    say(f"table check: {got} (host count {expect})")
+    assert got == expect
+    # with q_len 5 the length-0 sequence stays bad and nothing else changes
+    assert api.attn_paged_check_tables(tab.to(dev), lens.to(dev), nb, min_len=5) == \
+        _count_bad_entries(tab.tolist(), lens.tolist(), 5, nb)
+
+
 @pytest.mark.parametrize("S,D", [(1, 128), (3, 128), (16, 128), (1024, 128), (7, 64)])
 def test_lse_merge(api, S, D):
     g = torch.Generator().manual_seed(S)
