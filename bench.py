@@ -31,8 +31,9 @@ each with its own roofline entry (MFMA TFLOP/s or HBM GB/s); and
     nontemporal like the paged kernels; random 4 KiB also with the default
     cache policy).
 Each prefill and paged decode entry also carries ``cache_control``: the median
-single-launch time with warm caches and after a 512 MiB scratch write that
-evicts the MALL, so that the timed rate can be read against a cold-cache one.
+single-launch time with warm caches and after a 512 MiB pass that evicts the
+MALL, so that the timed rate can be read against a cold-cache one. It runs
+before the warm-up and the timed launches, and not under ``--only``.
 The
 ``cpu_baseline`` leg times the float64 CPU oracle on a bounded sample of the
 c2 workload on this host's cores.
@@ -118,6 +119,7 @@ def time_launches(torch, fn, warmup, steps):
 
 
 FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB last-level (MALL) cache
+WITH_CACHE_CONTROL = True  # off for --only, the single-workload runs the profiler traces
 
 
 def cache_control(torch, fn, calls=20):
@@ -248,8 +250,8 @@ def bench_prefill(torch, api, spec, warmup, steps, key):
         if fn(*args) != 0:
             raise RuntimeError("attn_prefill failed")
 
+    control = cache_control(torch, call) if WITH_CACHE_CONTROL else None
     kernel_ms, wall = time_launches(torch, call, warmup, steps)
-    control = cache_control(torch, call)
     flops = prefill_flops(spec.B, spec.H, spec.L, spec.D, spec.causal)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     traffic = load_traffic(key, source_digest(*KERNEL_SOURCES["prefill"]))
@@ -331,8 +333,8 @@ def bench_paged(torch, api, spec, warmup, steps, key):
         if fn(*args) != 0:
             raise RuntimeError("paged decode failed")
 
+    control = cache_control(torch, call) if WITH_CACHE_CONTROL else None
     ms, wall = time_launches(torch, call, warmup, steps)
-    control = cache_control(torch, call)
     # K and V bytes of every visible token, as the sequences address them
     kv = 2.0 * H * D * 2 * sum(lens)
     # bytes that must come from HBM: the shared prefix blocks are read once
@@ -385,8 +387,8 @@ def bench_paged_prefill(torch, api, spec, warmup, steps, key):
         if fn(*args) != 0:
             raise RuntimeError("attn_paged_prefill failed")
 
+    control = cache_control(torch, call) if WITH_CACHE_CONTROL else None
     ms, wall = time_launches(torch, call, warmup, steps)
-    control = cache_control(torch, call)
     # visible (query, key) pairs: query t of a sequence of n keys sees n - q_len + t + 1
     pairs = 0
     for n in inp.seq_lens.tolist():
@@ -446,8 +448,8 @@ def bench_paged_fp8(torch, api, spec, warmup, steps, key):
         if fn(*args) != 0:
             raise RuntimeError("attn_paged_decode_fp8 failed")
 
+    control = cache_control(torch, call) if WITH_CACHE_CONTROL else None
     ms, wall = time_launches(torch, call, warmup, steps)
-    control = cache_control(torch, call)
     # one byte per cached K and V value, plus the two scales of each (block, head)
     blocks = sum(-(-n // 16) for n in lens)
     kv = 2.0 * H * D * sum(lens) + 2.0 * 4 * H * blocks
@@ -609,6 +611,8 @@ def main():
         "probe": lambda: bench_probe(torch, api, 3, 20),
     }
     if args.only:
+        global WITH_CACHE_CONTROL
+        WITH_CACHE_CONTROL = False
         print(json.dumps({"only": args.only, **runners[args.only]()}), flush=True)
         return
 
