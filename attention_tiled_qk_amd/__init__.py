@@ -179,6 +179,22 @@ def attn_prefill(q, k, v, *, causal=True, scale=None, o=None, lse=None, return_l
     return (o, lse) if (return_lse or lse is not None) else o
 
 
+# With ATTN_CHECK_TABLES=1 in the environment, every paged call first counts
+# on the device the table entries it would read out of range and raises
+# instead of launching (a debugging mode: it waits for the count each call).
+CHECK_TABLES = os.environ.get("ATTN_CHECK_TABLES", "0") == "1"
+
+
+def _check_tables(block_tables, seq_lens, num_blocks, min_len, what, stream):
+    if not CHECK_TABLES:
+        return
+    n_len, n_id = attn_paged_check_tables(block_tables, seq_lens, num_blocks, min_len=min_len,
+                                          stream=stream)
+    if n_len or n_id:
+        raise ValueError(f"{what}: {n_len} sequence length(s) out of range and {n_id} block id(s) "
+                         f"outside [0, {num_blocks}) in the tables (ATTN_CHECK_TABLES)")
+
+
 def attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits=0):
     return int(lib.attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits))
 
@@ -230,6 +246,7 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
               _ptr(lse), B)
     tail = (q_len, D, nblk, width, bs, int(bool(causal)), float(scale), int(num_splits),
             _ptr(workspace), ws_bytes, ATTN_BF16, _stream(q.device, stream))
+    _check_tables(block_tables, seq_lens, nblk, q_len, "attn_paged_decode", stream)
     if Hq == Hkv:
         st = lib.attn_paged_decode(*common, Hq, *tail)
         _check(st, "attn_paged_decode")
@@ -274,6 +291,7 @@ def attn_paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True
         lse = torch.empty((B, H, q_len), device=q.device, dtype=torch.float32)
     if lse is not None:
         _dev(lse, "lse", torch.float32)
+    _check_tables(block_tables, seq_lens, nblk, q_len, "attn_paged_prefill", stream)
     st = lib.attn_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                                 _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, q_len, D, nblk,
                                 block_tables.shape[1], bs, int(bool(causal)), float(scale),
@@ -319,6 +337,7 @@ def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_le
             _ptr(cu_q_lens), _ptr(o), _ptr(lse), B, H)
     tail = (total_q, int(max_q_len), D, nblk, block_tables.shape[1], bs, int(bool(causal)),
             float(scale), ATTN_BF16, _stream(q.device, stream))
+    _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_prefill_varlen", stream)
     if Hp == H:
         _check(lib.attn_paged_prefill_varlen(*head, *tail), "attn_paged_prefill_varlen")
     else:
@@ -367,6 +386,7 @@ def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, st
     if out is None:
         out = torch.zeros((B, H, max_seq_len, D), device=pool.device, dtype=torch.bfloat16)
     _dev(out, "out", torch.bfloat16)
+    _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_gather", stream)
     st = lib.attn_paged_gather(_ptr(pool), _ptr(block_tables), _ptr(seq_lens), _ptr(out), B, H, D,
                                nblk, width, max_seq_len, _stream(pool.device, stream))
     _check(st, "attn_paged_gather")
@@ -430,6 +450,7 @@ def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, s
         raise ValueError("pool heads / head_dim must match the new tokens")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_append", stream)
     st = lib.attn_paged_append(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                _ptr(block_tables), _ptr(seq_lens), B, H, n_new, D, nblk,
                                block_tables.shape[1], bs, ATTN_BF16,
@@ -480,6 +501,7 @@ def attn_paged_append_fp8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_
     B, _, n_new, _ = k_new.shape
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_append_fp8", stream)
     st = lib.attn_paged_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                    _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                    _ptr(seq_lens), B, H, n_new, D, nblk, block_tables.shape[1],
@@ -530,6 +552,7 @@ def attn_paged_decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check_tables(block_tables, seq_lens, nblk, q_len, "attn_paged_decode_fp8", stream)
     st = lib.attn_paged_decode_fp8(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
                                    _ptr(v_scale), _ptr(block_tables), _ptr(seq_lens), _ptr(o),
                                    _ptr(lse), B, Hq, Hkv, q_len, D, nblk, width, bs,

@@ -758,6 +758,48 @@ def test_check_tables_counts_out_of_range_entries(api):
         _count_bad_entries(tab.tolist(), lens.tolist(), 5, nb)
 
 
+def test_check_tables_mode_refuses_bad_tables(api, monkeypatch):
+    """With the debugging switch on (ATTN_CHECK_TABLES=1), paged calls with valid
+    tables give the unchecked results, and a table entry past the pool makes
+    decode, prefill, append and gather raise before anything is launched. The
+    pools passed are views of the first N blocks of N + 1, so even the refused
+    id lies in allocated memory."""
+    H, D = 4, 128
+    lens = [100, 300]
+    need = [(n + 15) // 16 for n in lens]
+    N = sum(need)
+    g = torch.Generator().manual_seed(95)
+    dev = torch.device("cuda")
+    k_all = torch.randn(N + 1, H, 16, D, generator=g).to(torch.bfloat16).to(dev)
+    v_all = torch.randn(N + 1, H, 16, D, generator=g).to(torch.bfloat16).to(dev)
+    k, v = k_all[:N], v_all[:N]
+    q = torch.randn(2, H, 1, D, generator=g).to(torch.bfloat16).to(dev)
+    tab = torch.full((2, max(need)), -1, dtype=torch.int32)
+    c = 0
+    for b, n in enumerate(need):
+        for j in range(n):
+            tab[b, j] = c
+            c += 1
+    seq = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ref = api.attn_paged_decode(q, k, v, tab.to(dev), seq)
+    monkeypatch.setattr(api, "CHECK_TABLES", True)
+    assert torch.equal(api.attn_paged_decode(q, k, v, tab.to(dev), seq), ref)
+    bad = tab.clone()
+    bad[1, 0] = N
+    bad = bad.to(dev)
+    assert api.attn_paged_check_tables(bad, seq, N) == (0, 1)
+    with pytest.raises(ValueError, match="ATTN_CHECK_TABLES"):
+        api.attn_paged_decode(q, k, v, bad, seq)
+    with pytest.raises(ValueError, match="ATTN_CHECK_TABLES"):
+        api.attn_paged_prefill(q, k, v, bad, seq)
+    with pytest.raises(ValueError, match="ATTN_CHECK_TABLES"):
+        api.attn_paged_append(q, q, k, v, bad, seq)
+    with pytest.raises(ValueError, match="ATTN_CHECK_TABLES"):
+        api.attn_paged_gather(k, bad, seq, 320)
+    torch.cuda.synchronize()
+    assert torch.equal(k_all[:N], k) and torch.isfinite(k_all.float()).all()
+
+
 @pytest.mark.parametrize("S,D", [(1, 128), (3, 128), (16, 128), (1024, 128), (7, 64)])
 def test_lse_merge(api, S, D):
     g = torch.Generator().manual_seed(S)
