@@ -30,6 +30,8 @@ from .attention import (  # noqa: F401
     masked_attention,
     dense_attention,
     prefill,
+    block_state,
+    combine_states,
     online_softmax_attention,
     paged_gather,
     paged_attention,

@@ -105,21 +105,51 @@ def prefill(q, k, v, scale, causal, heads=None):
     return o, lse
 
 
+def block_state(q, k, v, scale, visible):
+    """Softmax state of one set of keys: (m, l, O) per query row.
+
+    m is the largest visible score of the row, l the sum of exp(s - m) over
+    its visible keys and O the sum of exp(s - m) v_j (unnormalised). A row
+    that sees none of these keys has m = -inf, l = 0, O = 0. The softmax
+    result over the keys is O / l with log-sum-exp m + log l.
+    """
+    s = scale * (q @ k.T)
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1) if k.shape[0] > 0 else np.full(q.shape[0], -np.inf)
+    m_ref = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(visible, np.exp(s - m_ref[:, None]), 0.0)
+    return m, e.sum(axis=1), e @ v
+
+
+def combine_states(a, b):
+    """The state over the union of two disjoint key sets.
+
+    With M = max(m_a, m_b), both states are brought to the common reference:
+    l = e^(m_a - M) l_a + e^(m_b - M) l_b and O likewise, since
+    exp(s - m_a) e^(m_a - M) = exp(s - M) for every key. The operation is
+    associative and commutative, which is why the key range may be cut into
+    tiles and folded in any grouping ([P1] §2.2: the tiled result equals the
+    softmax over the whole row). A side with m = -inf contributes 0, and
+    -inf - (-inf) is never formed.
+    """
+    (ma, la, oa), (mb, lb, ob) = a, b
+    m = np.maximum(ma, mb)
+    m_ref = np.where(np.isfinite(m), m, 0.0)
+    wa = np.where(np.isfinite(ma), np.exp(ma - m_ref), 0.0)
+    wb = np.where(np.isfinite(mb), np.exp(mb - m_ref), 0.0)
+    return m, wa * la + wb * lb, wa[:, None] * oa + wb[:, None] * ob
+
+
 def online_softmax_attention(q, k, v, scale, causal, bm, bn):
-    """Tiled attention with the online-softmax recurrence, in float64.
+    """Tiled attention: per-tile softmax states folded into a running state.
 
-    Follows the FlashAttention tiling of [P1] §2.2: Q is cut into row blocks of
-    ``bm`` rows (outer loop, as FlashAttention-2 orders it in [P3]) and K, V into
-    blocks of ``bn`` keys (inner loop). Each row keeps a running maximum m, a
-    running exponential sum l and an unnormalised output O. For each key block:
-    the block's scores are formed, the new maximum is the larger of the old one
-    and the block's row maximum, the old l and O are scaled by exp(m_old - m_new),
-    the block's exp(S - m_new) is added to l and its product with V_j to O. The
-    division by l happens once per row block, after its last key block.
-
-    Starting state m = -inf, l = 0, O = 0. A factor exp(m_old - m_new) with
-    m_old = -inf is 0; -inf - (-inf) is never evaluated (a fully masked block
-    leaves the state untouched). Returns (o [Lq, Dv], lse [Lq]).
+    The tiling of [P1] §2.2: Q is cut into row blocks of ``bm`` rows (the outer
+    loop, as FlashAttention-2 orders it in [P3]) and K, V into blocks of ``bn``
+    keys. Each key block's own state (block_state) is folded into the row
+    block's running state with combine_states, in key order, starting from the
+    empty state (m = -inf, l = 0, O = 0); O / l is formed once per row block
+    after its last key block. Returns (o [Lq, Dv], lse [Lq]); rows that see no
+    key give o = 0, lse = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     lq, lk = q.shape[0], k.shape[0]
@@ -128,22 +158,12 @@ def online_softmax_attention(q, k, v, scale, causal, bm, bn):
     lse = np.full(lq, -np.inf)
     for r0 in range(0, lq, bm):
         r1 = min(r0 + bm, lq)
-        m = np.full(r1 - r0, -np.inf)
-        l = np.zeros(r1 - r0)
-        acc = np.zeros((r1 - r0, v.shape[1]))
+        state = (np.full(r1 - r0, -np.inf), np.zeros(r1 - r0), np.zeros((r1 - r0, v.shape[1])))
         for c0 in range(0, lk, bn):
             c1 = min(c0 + bn, lk)
-            vis = vis_all[r0:r1, c0:c1]
-            s = scale * (q[r0:r1] @ k[c0:c1].T)
-            s = np.where(vis, s, -np.inf)
-            m_new = np.maximum(m, s.max(axis=1))
-            live = np.isfinite(m_new)
-            m_ref = np.where(live, m_new, 0.0)
-            alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
-            p = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
-            l = alpha * l + p.sum(axis=1)
-            acc = alpha[:, None] * acc + p @ v[c0:c1]
-            m = m_new
+            tile = block_state(q[r0:r1], k[c0:c1], v[c0:c1], scale, vis_all[r0:r1, c0:c1])
+            state = combine_states(state, tile)
+        m, l, acc = state
         done = l > 0
         out[r0:r1] = np.where(done[:, None], acc / np.where(done, l, 1.0)[:, None], 0.0)
         lse[r0:r1] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)

@@ -81,43 +81,52 @@ def test_dense_mutant_caught(bug):
 
 
 def _online_variant(q, k, v, scale, causal, bm, bn, bug):
+    """A copy of the oracle's tiled attention (per-tile states folded with the
+    log-sum-exp combination) with one planted mistake."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     lq, lk = q.shape[0], k.shape[0]
     vis_all = (np.arange(lk)[None, :] <= (lk - lq) + np.arange(lq)[:, None]) if causal \
         else np.ones((lq, lk), dtype=bool)
+
+    def tile_state(r0, r1, c0, c1):
+        vis = vis_all[r0:r1, c0:c1]
+        s = np.where(vis, scale * (q[r0:r1] @ k[c0:c1].T), -np.inf)
+        m = s.max(axis=1)
+        m_ref = np.where(np.isfinite(m), m, 0.0)
+        e = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
+        o = e @ v[c0:c1]
+        if bug == "normalise_each_tile":
+            o = o / np.where(e.sum(axis=1) > 0, e.sum(axis=1), 1.0)[:, None]
+        return m, e.sum(axis=1), o
+
+    def combine(a, b):
+        (ma, la, oa), (mb, lb, ob) = a, b
+        m = np.maximum(ma, mb)
+        m_ref = np.where(np.isfinite(m), m, 0.0)
+        if bug == "weight_sign":
+            wa = np.where(np.isfinite(ma), np.exp(m_ref - ma), 0.0)
+        else:
+            wa = np.where(np.isfinite(ma), np.exp(ma - m_ref), 0.0)
+        wb = np.where(np.isfinite(mb), np.exp(mb - m_ref), 0.0)
+        l = (la + wb * lb) if bug == "no_rescale_l" else (wa * la + wb * lb)
+        o = (oa + wb[:, None] * ob) if bug == "no_rescale_o" else (wa[:, None] * oa + wb[:, None] * ob)
+        return m, l, o
+
     out = np.zeros((lq, v.shape[1]))
     lse = np.full(lq, -np.inf)
     for r0 in range(0, lq, bm):
         r1 = min(r0 + bm, lq)
-        m = np.full(r1 - r0, -np.inf)
-        l = np.zeros(r1 - r0)
-        acc = np.zeros((r1 - r0, v.shape[1]))
+        state = (np.full(r1 - r0, -np.inf), np.zeros(r1 - r0), np.zeros((r1 - r0, v.shape[1])))
         for c0 in range(0, lk, bn):
-            c1 = min(c0 + bn, lk)
-            vis = vis_all[r0:r1, c0:c1]
-            s = np.where(vis, scale * (q[r0:r1] @ k[c0:c1].T), -np.inf)
-            m_new = np.maximum(m, s.max(axis=1))
-            m_ref = np.where(np.isfinite(m_new), m_new, 0.0)
-            if bug == "alpha_sign":
-                alpha = np.where(np.isfinite(m), np.exp(m_ref - m), 0.0)
-            else:
-                alpha = np.where(np.isfinite(m), np.exp(m - m_ref), 0.0)
-            p = np.where(vis, np.exp(s - m_ref[:, None]), 0.0)
-            l = (l if bug == "no_rescale_l" else alpha * l) + p.sum(axis=1)
-            acc = (acc if bug == "no_rescale_o" else alpha[:, None] * acc) + p @ v[c0:c1]
-            m = m_new
-            if bug == "normalise_each_tile":
-                acc = acc / np.where(l > 0, l, 1.0)[:, None]
+            state = combine(state, tile_state(r0, r1, c0, min(c0 + bn, lk)))
+        m, l, acc = state
         done = l > 0
-        if bug == "normalise_each_tile":
-            out[r0:r1] = acc
-        else:
-            out[r0:r1] = np.where(done[:, None], acc / np.where(done, l, 1.0)[:, None], 0.0)
+        out[r0:r1] = np.where(done[:, None], acc / np.where(done, l, 1.0)[:, None], 0.0)
         lse[r0:r1] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)
     return out, lse
 
 
-@pytest.mark.parametrize("bug", ["alpha_sign", "no_rescale_l", "no_rescale_o", "normalise_each_tile"])
+@pytest.mark.parametrize("bug", ["weight_sign", "no_rescale_l", "no_rescale_o", "normalise_each_tile"])
 def test_online_mutant_caught(bug):
     fn = lambda q, k, v, s, c: _online_variant(q, k, v, s, c, 2, 3, None)  # noqa: E731
     assert not _fails_some(ALL_CHECKS, fn)

@@ -195,6 +195,31 @@ def test_tiled_online_softmax_equals_one_shot(bm, bn, lq, lk, causal):
     np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
 
 
+def test_state_combination_is_associative_and_exact():
+    """Folding per-block states in any grouping or order gives the one-shot
+    softmax over all keys: ((a b) c) == (a (b c)) == (c (a b)), and O / l,
+    m + log l equal dense attention over the union of the blocks."""
+    rng = np.random.default_rng(17)
+    q, k, v = rnd(rng, 9, 8), rnd(rng, 30, 8), rnd(rng, 30, 8)
+    vis = oracle.causal_visibility(9, 30)
+    cut = [(0, 7), (7, 19), (19, 30)]
+    a, b, c = (oracle.block_state(q, k[x:y], v[x:y], 0.7, vis[:, x:y]) for x, y in cut)
+    left = oracle.combine_states(oracle.combine_states(a, b), c)
+    right = oracle.combine_states(a, oracle.combine_states(b, c))
+    swapped = oracle.combine_states(c, oracle.combine_states(b, a))
+    o_ref, lse_ref = oracle.dense_attention(q, k, v, 0.7, True)
+    for m, l, o in (left, right, swapped):
+        np.testing.assert_allclose(o / l[:, None], o_ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(m + np.log(l), lse_ref, rtol=0, atol=1e-13)
+    # the empty state is the identity; a block no row sees leaves a state unchanged
+    empty = (np.full(9, -np.inf), np.zeros(9), np.zeros((9, 8)))
+    for x, y in zip(oracle.combine_states(empty, a), a):
+        np.testing.assert_array_equal(x, y)
+    masked = oracle.block_state(q, k, v, 0.7, np.zeros((9, 30), dtype=bool))
+    for x, y in zip(oracle.combine_states(a, masked), a):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_online_softmax_pins():
     """The tiled recurrence also passes the definition pins on its own."""
     for bm, bn in [(2, 3), (1, 1), (4, 4)]:
