@@ -16,14 +16,16 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-    # packed fp32 VALU forms are kept out of the generated code
+    # packed fp32 VALU forms are kept out of the generated code. hipcc forwards
+    # -Xclang to the host pass too (-Xarch_device refuses options that take an
+    # argument), where LLVM prints that it ignores the unknown feature.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Werror", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = [
     "attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "paged.hip", "kv_append.hip",
-    "kv_cache.hip", "probe.hip", "table_check.hip",
+    "kv_cache.hip", "table_check.hip",
 ]
 
 
@@ -34,13 +36,24 @@ def _hipcc():
     return exe
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, src_dir=CSRC, build_dir=BUILD_DIR):
+    obj = os.path.join(build_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(src_dir, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
+
+
+def link(objs, lib_path):
+    """Link objects into the shared library lib_path (replaced atomically)."""
+    tmp = lib_path + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def build(verbose=True):
@@ -48,12 +61,7 @@ def build(verbose=True):
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    link(objs, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}", file=sys.stderr)
     return LIB_PATH

@@ -27,7 +27,7 @@ The same run also measures, under ``secondary``:
 each with its own roofline entry (MFMA TFLOP/s or HBM GB/s); and
   * probe: the read bandwidth HBM sustains for the paged kernels' access
     patterns -- 4 KiB and 2 KiB blocks of a 2.5 GiB buffer in random order,
-    and 4 KiB blocks in address order (attn_probe_block_read, loads only,
+    and 4 KiB blocks in address order (probe/, a library of its own: loads only,
     nontemporal like the paged kernels; random 4 KiB also with the default
     cache policy).
 Each prefill and paged decode entry also carries ``cache_control``: the median
@@ -538,10 +538,12 @@ def bench_copy(torch, warmup, steps):
 
 
 def bench_probe(torch, api, warmup, steps):
+    import probe
     """Read-bandwidth ceilings of the paged kernels' access patterns: whole
     blocks of a 2.5 GiB buffer read in a random order -- 4 KiB, one bf16 cache
     slab of a (block, head) at D = 128, and 2 KiB, one FP8 slab -- and in
-    address order, through attn_probe_block_read (loads only, 8192 waves),
+    address order, through the probe library's probe_block_read (loads only,
+    8192 waves),
     with nontemporal loads (the policy of the paged kernels) and, for the
     random 4 KiB case, the default policy too."""
     total = 5 << 29
@@ -559,7 +561,7 @@ def bench_probe(torch, api, warmup, steps):
         ids = torch.randperm(n, generator=g) if shuffled else torch.arange(n)
         order = ids.to(torch.int32).cuda()
         ms, _ = time_launches(
-            torch, lambda: api.attn_probe_block_read(buf, bb, order, n_waves, nontemporal=nt, sink=sink),
+            torch, lambda: probe.probe_block_read(buf, bb, order, n_waves, nontemporal=nt, sink=sink),
             warmup, steps)
         gbs = total / (ms * 1e-3) / 1e9
         log(f"[bench] read probe {name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%})")

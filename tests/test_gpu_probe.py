@@ -1,4 +1,5 @@
-"""GPU check of the read-bandwidth probe (attn_probe_block_read).
+"""GPU check of the benchmark's read-bandwidth probe (probe.probe_block_read,
+built into its own library, libattn_probe.so).
 
 The probe computes nothing but an XOR of every 32-bit word it reads, so its
 result has a plain definition: the XOR over all sink words must equal the XOR
@@ -19,8 +20,8 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module")
 def api():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
-    import attention_tiled_qk_amd as m
-    return m
+    import probe
+    return probe
 
 
 def host_xor(data, block_bytes, order):
@@ -42,7 +43,7 @@ def test_probe_xor_matches_host(api, block_bytes, n_reads, n_waves, nontemporal)
     order = torch.randint(0, nb, (n_reads,), generator=g, dtype=torch.int32)
     print(f"[probe test] block_bytes={block_bytes} n_reads={n_reads} n_waves={n_waves} "
           f"nontemporal={nontemporal}", flush=True)
-    sink = api.attn_probe_block_read(data.cuda(), block_bytes, order.cuda(), n_waves,
+    sink = api.probe_block_read(data.cuda(), block_bytes, order.cuda(), n_waves,
                                      nontemporal=nontemporal)
     torch.cuda.synchronize()
     assert device_xor(sink) == host_xor(data, block_bytes, order)
@@ -53,6 +54,6 @@ def test_probe_repeated_ids_cancel(api):
     data = torch.randint(0, 256, (8 * block_bytes,), generator=torch.Generator().manual_seed(3),
                          dtype=torch.uint8)
     order = torch.tensor([2, 5, 2, 5], dtype=torch.int32)
-    sink = api.attn_probe_block_read(data.cuda(), block_bytes, order.cuda(), 4)
+    sink = api.probe_block_read(data.cuda(), block_bytes, order.cuda(), 4)
     torch.cuda.synchronize()
     assert device_xor(sink) == 0
