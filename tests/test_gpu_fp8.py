@@ -264,12 +264,11 @@ def test_decode_fp8_of_appended_tokens(api):
     assert np.abs(ro[0, 0] - rb).max() < 0.1
 
 
-def test_decode_fp8_full_size_sampled(api):
+def test_decode_fp8_full_size(api):
     inp = paged_inputs_fp8(C4F8)
-    pairs = [(0, 0), (17, 21), (63, 39)]
     o, lse = _run(api, inp, C4F8.num_splits)
-    ro, rl = _ref(inp, heads=pairs)
-    e, el = _err(o, lse, ro, rl, pairs)
-    say(f"  fp8 decode full size max|dO|={e:.3e} max|dlse|={el:.3e}")
+    ro, rl = _ref(inp)
+    e, el = _err(o, lse, ro, rl)
+    say(f"  fp8 decode full size, all pairs: max|dO|={e:.3e} max|dlse|={el:.3e}")
     assert torch.isfinite(o.float()).all()
     assert e <= TOL_BF16 and el <= TOL_LSE
