@@ -22,7 +22,8 @@ __all__ = [
     "attn_paged_prefill_varlen", "attn_paged_prefill_gqa",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
     "KVCacheAllocator", "attn_paged_append_fp8", "attn_paged_copy_blocks_fp8",
-    "attn_paged_decode_fp8", "attn_probe_block_read", "attn_paged_check_tables", "attn_version",
+    "attn_paged_decode_fp8", "attn_paged_check_tables", "attn_paged_check_append",
+    "attn_paged_check_ragged", "attn_paged_check_ids", "attn_version",
     "lib", "LIB_PATH",
     "ATTN_F32", "ATTN_BF16",
 ]
@@ -69,8 +70,12 @@ lib.attn_paged_gather.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_gather.restype = _i
 lib.attn_paged_check_tables.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p]
 lib.attn_paged_check_tables.restype = _i
-lib.attn_probe_block_read.argtypes = [_p, _i, _i, _p, _i, _p, _i, _i, _p]
-lib.attn_probe_block_read.restype = _i
+lib.attn_paged_check_append.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p]
+lib.attn_paged_check_append.restype = _i
+lib.attn_paged_check_ragged.argtypes = [_p, _p, _i, _i, _i, _p, _p]
+lib.attn_paged_check_ragged.restype = _i
+lib.attn_paged_check_ids.argtypes = [_p, _p, _i, _i, _p, _p]
+lib.attn_paged_check_ids.restype = _i
 lib.attn_paged_append.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
 lib.attn_paged_append.restype = _i
 lib.attn_paged_copy_blocks.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
@@ -122,16 +127,43 @@ def _check(status, where):
         raise AttnError(status, where)
 
 
-def _dev(t, name, dtype=None):
+# Device type the tensors passed to the library must have. Only the binding's
+# own CPU tests change it, to check argument validation without a GPU (with a
+# stub in place of ``lib``, so nothing is launched).
+_DEVICE_TYPE = "cuda"
+
+
+def _dev(t, name, dtype=None, device=None, shape=None):
+    """Check that t is a contiguous device tensor (of dtype, on device, of
+    exactly shape, where given) and return it."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     return t
+
+
+def _workspace(ws, need, device):
+    """The split-KV scratch: allocated here when none is given and one is
+    needed; a caller's tensor must be contiguous, on `device` and hold at
+    least `need` bytes (any dtype). Returns (tensor or None, its bytes)."""
+    if ws is None:
+        if need <= 0:
+            return None, 0
+        ws = torch.empty(need // 4, device=device, dtype=torch.float32)
+    _dev(ws, "workspace", device=device)
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return ws, nbytes
 
 
 def _ptr(t):
@@ -158,20 +190,20 @@ def attn_prefill(q, k, v, *, causal=True, scale=None, o=None, lse=None, return_l
     Returns o (and the float32 log-sum-exp [B, H, L] when ``return_lse``).
     """
     _dev(q, "q")
-    _dev(k, "k", q.dtype)
-    _dev(v, "v", q.dtype)
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+    if q.dim() != 4:
         raise ValueError("q, k, v must all be [B, H, L, D] of the same shape")
+    _dev(k, "k", q.dtype, q.device, q.shape)
+    _dev(v, "v", q.dtype, q.device, q.shape)
     B, H, L, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if o is None:
         o = torch.empty_like(q)
-    _dev(o, "o", q.dtype)
+    _dev(o, "o", q.dtype, q.device, q.shape)
     if return_lse and lse is None:
         lse = torch.empty((B, H, L), device=q.device, dtype=torch.float32)
     if lse is not None:
-        _dev(lse, "lse", torch.float32)
+        _dev(lse, "lse", torch.float32, q.device, (B, H, L))
     st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, L, D,
                           int(bool(causal)), float(scale), _dtype_code(q.dtype),
                           _stream(q.device, stream))
@@ -195,6 +227,33 @@ def _check_tables(block_tables, seq_lens, num_blocks, min_len, what, stream):
                          f"outside [0, {num_blocks}) in the tables (ATTN_CHECK_TABLES)")
 
 
+def _check_append_tables(block_tables, seq_lens, num_blocks, n_new, what, stream):
+    if not CHECK_TABLES:
+        return
+    n_len, n_id = attn_paged_check_append(block_tables, seq_lens, num_blocks, n_new, stream=stream)
+    if n_len or n_id:
+        raise ValueError(f"{what}: {n_len} sequence length(s) out of range and {n_id} written "
+                         f"block id(s) neither -1 nor in [0, {num_blocks}) (ATTN_CHECK_TABLES)")
+
+
+def _check_ragged(cu_q_lens, seq_lens, total_q, max_q_len, what, stream):
+    if not CHECK_TABLES:
+        return
+    n_off, n_seq = attn_paged_check_ragged(cu_q_lens, seq_lens, total_q, max_q_len, stream=stream)
+    if n_off or n_seq:
+        raise ValueError(f"{what}: {n_off} query offset error(s) and {n_seq} sequence(s) with more "
+                         f"queries than max_q_len or their length (ATTN_CHECK_TABLES)")
+
+
+def _check_ids(src, dst, num_blocks, what, stream):
+    if not CHECK_TABLES:
+        return
+    n_src, n_dst = attn_paged_check_ids(src, dst, num_blocks, stream=stream)
+    if n_src or n_dst:
+        raise ValueError(f"{what}: {n_src} src and {n_dst} dst block id(s) outside "
+                         f"[0, {num_blocks}) (ATTN_CHECK_TABLES)")
+
+
 def attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits=0):
     return int(lib.attn_paged_workspace_bytes(B, H, q_len, D, max_blocks_per_seq, num_splits))
 
@@ -216,10 +275,11 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
     attn_paged_decode_gqa (grouped-query attention).
     """
     _dev(q, "q", torch.bfloat16)
-    _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    dev = q.device
+    _dev(k_pool, "k_pool", torch.bfloat16, dev)
+    _dev(v_pool, "v_pool", torch.bfloat16, dev)
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
     if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [B, Hq, q_len, D] and the pools [num_blocks, Hkv, 16, D]")
     B, Hq, q_len, D = q.shape
@@ -233,15 +293,13 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
         scale = 1.0 / math.sqrt(D)
     if o is None:
         o = torch.empty_like(q)
-    _dev(o, "o", torch.bfloat16)
+    _dev(o, "o", torch.bfloat16, dev, q.shape)
     if return_lse and lse is None:
-        lse = torch.empty((B, Hq, q_len), device=q.device, dtype=torch.float32)
+        lse = torch.empty((B, Hq, q_len), device=dev, dtype=torch.float32)
     if lse is not None:
-        _dev(lse, "lse", torch.float32)
+        _dev(lse, "lse", torch.float32, dev, (B, Hq, q_len))
     need = attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, width, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     common = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), _ptr(o),
               _ptr(lse), B)
     tail = (q_len, D, nblk, width, bs, int(bool(causal)), float(scale), int(num_splits),
@@ -270,10 +328,11 @@ def attn_paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True
     q_len newest tokens of each sequence, attend its seq_lens[b] cached keys in
     k_pool, v_pool [num_blocks, H, 16, D] through block_tables [B, W] int32."""
     _dev(q, "q", torch.bfloat16)
-    _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    dev = q.device
+    _dev(k_pool, "k_pool", torch.bfloat16, dev)
+    _dev(v_pool, "v_pool", torch.bfloat16, dev)
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
     if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [B, H, q_len, D] and the pools [num_blocks, H, 16, D]")
     B, H, q_len, D = q.shape
@@ -286,11 +345,11 @@ def attn_paged_prefill(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True
         scale = 1.0 / math.sqrt(D)
     if o is None:
         o = torch.empty_like(q)
-    _dev(o, "o", torch.bfloat16)
+    _dev(o, "o", torch.bfloat16, dev, q.shape)
     if return_lse and lse is None:
-        lse = torch.empty((B, H, q_len), device=q.device, dtype=torch.float32)
+        lse = torch.empty((B, H, q_len), device=dev, dtype=torch.float32)
     if lse is not None:
-        _dev(lse, "lse", torch.float32)
+        _dev(lse, "lse", torch.float32, dev, (B, H, q_len))
     _check_tables(block_tables, seq_lens, nblk, q_len, "attn_paged_prefill", stream)
     st = lib.attn_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                                 _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, q_len, D, nblk,
@@ -310,11 +369,12 @@ def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_le
     fewer heads than q (a divisor of them), the call goes to
     attn_paged_prefill_gqa (grouped-query attention)."""
     _dev(q, "q", torch.bfloat16)
-    _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
-    _dev(cu_q_lens, "cu_q_lens", torch.int32)
+    dev = q.device
+    _dev(k_pool, "k_pool", torch.bfloat16, dev)
+    _dev(v_pool, "v_pool", torch.bfloat16, dev)
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
+    _dev(cu_q_lens, "cu_q_lens", torch.int32, dev)
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [total_q, H, D] and the pools [num_blocks, H, 16, D]")
     total_q, H, D = q.shape
@@ -328,16 +388,17 @@ def attn_paged_prefill_varlen(q, k_pool, v_pool, block_tables, seq_lens, cu_q_le
         scale = 1.0 / math.sqrt(D)
     if o is None:
         o = torch.empty_like(q)
-    _dev(o, "o", torch.bfloat16)
+    _dev(o, "o", torch.bfloat16, dev, q.shape)
     if return_lse and lse is None:
-        lse = torch.empty((total_q, H), device=q.device, dtype=torch.float32)
+        lse = torch.empty((total_q, H), device=dev, dtype=torch.float32)
     if lse is not None:
-        _dev(lse, "lse", torch.float32)
+        _dev(lse, "lse", torch.float32, dev, (total_q, H))
     head = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens),
             _ptr(cu_q_lens), _ptr(o), _ptr(lse), B, H)
     tail = (total_q, int(max_q_len), D, nblk, block_tables.shape[1], bs, int(bool(causal)),
             float(scale), ATTN_BF16, _stream(q.device, stream))
     _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_prefill_varlen", stream)
+    _check_ragged(cu_q_lens, seq_lens, total_q, int(max_q_len), "attn_paged_prefill_varlen", stream)
     if Hp == H:
         _check(lib.attn_paged_prefill_varlen(*head, *tail), "attn_paged_prefill_varlen")
     else:
@@ -358,17 +419,18 @@ def attn_lse_merge(o_part, lse_part, *, out_dtype=torch.bfloat16, o=None, lse=No
                    return_lse=False, stream=None):
     """Merge o_part [B, H, q_len, S, D] / lse_part [B, H, q_len, S] (float32)."""
     _dev(o_part, "o_part", torch.float32)
-    _dev(lse_part, "lse_part", torch.float32)
+    dev = o_part.device
+    _dev(lse_part, "lse_part", torch.float32, dev)
     if o_part.dim() != 5 or lse_part.shape != o_part.shape[:4]:
         raise ValueError("o_part must be [B, H, q_len, S, D] and lse_part [B, H, q_len, S]")
     B, H, q_len, S, D = o_part.shape
     if o is None:
-        o = torch.empty((B, H, q_len, D), device=o_part.device, dtype=out_dtype)
-    _dev(o, "o")
+        o = torch.empty((B, H, q_len, D), device=dev, dtype=out_dtype)
+    _dev(o, "o", None, dev, (B, H, q_len, D))
     if return_lse and lse is None:
-        lse = torch.empty((B, H, q_len), device=o_part.device, dtype=torch.float32)
+        lse = torch.empty((B, H, q_len), device=dev, dtype=torch.float32)
     if lse is not None:
-        _dev(lse, "lse", torch.float32)
+        _dev(lse, "lse", torch.float32, dev, (B, H, q_len))
     st = lib.attn_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), B, H, q_len, S, D,
                             _dtype_code(o.dtype), _stream(o_part.device, stream))
     _check(st, "attn_lse_merge")
@@ -379,13 +441,18 @@ def attn_paged_gather(pool, block_tables, seq_lens, max_seq_len, *, out=None, st
     """Copy each sequence's valid rows out of pool [N, H, 16, D] (bf16) into
     out [B, H, max_seq_len, D]; rows past seq_len are left as they were."""
     _dev(pool, "pool", torch.bfloat16)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    dev = pool.device
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
+    if pool.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("pool must be [N, H, 16, D] and block_tables [B, W]")
     nblk, H, bs, D = pool.shape
     B, width = block_tables.shape
+    if seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be [B]")
     if out is None:
-        out = torch.zeros((B, H, max_seq_len, D), device=pool.device, dtype=torch.bfloat16)
-    _dev(out, "out", torch.bfloat16)
+        out = torch.zeros((B, H, max_seq_len, D), device=dev, dtype=torch.bfloat16)
+    _dev(out, "out", torch.bfloat16, dev, (B, H, max_seq_len, D))
     _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_gather", stream)
     st = lib.attn_paged_gather(_ptr(pool), _ptr(block_tables), _ptr(seq_lens), _ptr(out), B, H, D,
                                nblk, width, max_seq_len, _stream(pool.device, stream))
@@ -399,7 +466,9 @@ def attn_paged_check_tables(block_tables, seq_lens, num_blocks, *, min_len=1, st
     16 * width keys, table entries those calls read whose id lies outside
     [0, num_blocks)). Waits for the count (a debugging aid, not for hot loops)."""
     _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32, block_tables.device)
+    if block_tables.dim() != 2 or seq_lens.shape != (block_tables.shape[0],):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
     B, width = block_tables.shape
     bad = torch.empty(2, device=block_tables.device, dtype=torch.int32)
     st = lib.attn_paged_check_tables(_ptr(block_tables), _ptr(seq_lens), B, min_len, num_blocks, width,
@@ -409,26 +478,51 @@ def attn_paged_check_tables(block_tables, seq_lens, num_blocks, *, min_len=1, st
     return n_len, n_id
 
 
-def attn_probe_block_read(buf, block_bytes, order, n_waves, *, nontemporal=False, sink=None,
-                          stream=None):
-    """Read the blocks of buf (uint8, a multiple of block_bytes long) listed in
-    order (int32) and nothing else, with the default or the nontemporal cache
-    policy; returns sink [n_waves * 64] int32 whose XOR over all words is the
-    XOR of every 32-bit word read. A bandwidth probe."""
-    _dev(buf, "buf", torch.uint8)
-    _dev(order, "order", torch.int32)
-    if buf.numel() % block_bytes != 0:
-        raise ValueError("buf must hold a whole number of blocks")
-    if sink is None:
-        sink = torch.empty(n_waves * 64, device=buf.device, dtype=torch.int32)
-    _dev(sink, "sink", torch.int32)
-    if sink.numel() < n_waves * 64:
-        raise ValueError("sink must hold n_waves * 64 words")
-    st = lib.attn_probe_block_read(_ptr(buf), buf.numel() // block_bytes, block_bytes, _ptr(order),
-                                   order.numel(), _ptr(sink), n_waves, int(bool(nontemporal)),
-                                   _stream(buf.device, stream))
-    _check(st, "attn_probe_block_read")
-    return sink
+def _counts(fn, args, device, where, stream):
+    bad = torch.empty(2, device=device, dtype=torch.int32)
+    _check(fn(*args, _ptr(bad), _stream(device, stream)), where)
+    return tuple(bad.tolist())
+
+
+def attn_paged_check_append(block_tables, seq_lens, num_blocks, n_new, *, stream=None):
+    """Count, on the device, what an append of n_new tokens per sequence would
+    write out of range: returns (lengths outside [0, 16 * width], entries the
+    append writes through that are neither -1 nor in [0, num_blocks)). Waits
+    for the count."""
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32, block_tables.device)
+    if block_tables.dim() != 2 or seq_lens.shape != (block_tables.shape[0],):
+        raise ValueError("block_tables must be [B, W] and seq_lens [B]")
+    B, width = block_tables.shape
+    return _counts(lib.attn_paged_check_append,
+                   (_ptr(block_tables), _ptr(seq_lens), B, n_new, num_blocks, width),
+                   block_tables.device, "attn_paged_check_append", stream)
+
+
+def attn_paged_check_ragged(cu_q_lens, seq_lens, total_q, max_q_len, *, stream=None):
+    """Count, on the device, the errors of a ragged call's packed query offsets:
+    returns (offset errors -- cu[0] != 0, cu[B] != total_q, decreasing steps --,
+    sequences with more queries than max_q_len or than their length). Waits for
+    the count."""
+    _dev(cu_q_lens, "cu_q_lens", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32, cu_q_lens.device)
+    B = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
+    if B <= 0 or cu_q_lens.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q_lens [B + 1]")
+    return _counts(lib.attn_paged_check_ragged,
+                   (_ptr(cu_q_lens), _ptr(seq_lens), B, total_q, max_q_len),
+                   cu_q_lens.device, "attn_paged_check_ragged", stream)
+
+
+def attn_paged_check_ids(src, dst, num_blocks, *, stream=None):
+    """Count, on the device, the ids of src and of dst outside [0, num_blocks).
+    Waits for the count."""
+    _dev(src, "src", torch.int32)
+    _dev(dst, "dst", torch.int32, src.device)
+    if src.dim() != 1 or dst.shape != src.shape:
+        raise ValueError("src, dst must be 1-D of one length")
+    return _counts(lib.attn_paged_check_ids, (_ptr(src), _ptr(dst), src.numel(), num_blocks),
+                   src.device, "attn_paged_check_ids", stream)
 
 
 def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, stream=None):
@@ -436,11 +530,12 @@ def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, s
     in place: token t of sequence b goes to position seq_lens[b] - n_new + t
     (seq_lens counts the new tokens) through block_tables [B, W] int32."""
     _dev(k_new, "k_new", torch.bfloat16)
-    _dev(v_new, "v_new", torch.bfloat16)
-    _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    dev = k_new.device
+    _dev(v_new, "v_new", torch.bfloat16, dev)
+    _dev(k_pool, "k_pool", torch.bfloat16, dev)
+    _dev(v_pool, "v_pool", torch.bfloat16, dev)
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
     if k_new.dim() != 4 or v_new.shape != k_new.shape or k_pool.dim() != 4 \
             or v_pool.shape != k_pool.shape:
         raise ValueError("k_new, v_new must be [B, H, n_new, D] and the pools [N, H, 16, D]")
@@ -450,7 +545,7 @@ def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, s
         raise ValueError("pool heads / head_dim must match the new tokens")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, W] and seq_lens [B]")
-    _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_append", stream)
+    _check_append_tables(block_tables, seq_lens, nblk, n_new, "attn_paged_append", stream)
     st = lib.attn_paged_append(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                _ptr(block_tables), _ptr(seq_lens), B, H, n_new, D, nblk,
                                block_tables.shape[1], bs, ATTN_BF16,
@@ -461,24 +556,28 @@ def attn_paged_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, *, s
 def attn_paged_copy_blocks(k_pool, v_pool, src, dst, *, stream=None):
     """Copy physical block src[i] onto dst[i] in both pools (int32 device ids)."""
     _dev(k_pool, "k_pool", torch.bfloat16)
-    _dev(v_pool, "v_pool", torch.bfloat16)
-    _dev(src, "src", torch.int32)
-    _dev(dst, "dst", torch.int32)
+    dev = k_pool.device
+    _dev(v_pool, "v_pool", torch.bfloat16, dev)
+    _dev(src, "src", torch.int32, dev)
+    _dev(dst, "dst", torch.int32, dev)
     if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or src.dim() != 1 \
             or dst.shape != src.shape:
         raise ValueError("pools must be [N, H, 16, D] and src, dst 1-D of one length")
     nblk, H, _, D = k_pool.shape
+    if src.numel() > 0:
+        _check_ids(src, dst, nblk, "attn_paged_copy_blocks", stream)
     st = lib.attn_paged_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst),
                                     src.numel(), nblk, H, D, ATTN_BF16,
                                     _stream(k_pool.device, stream))
     _check(st, "attn_paged_copy_blocks")
 
 
-def _fp8_pools(k_pool, v_pool, k_scale, v_scale):
-    _dev(k_pool, "k_pool", torch.uint8)
-    _dev(v_pool, "v_pool", torch.uint8)
-    _dev(k_scale, "k_scale", torch.float32)
-    _dev(v_scale, "v_scale", torch.float32)
+def _fp8_pools(k_pool, v_pool, k_scale, v_scale, device=None):
+    _dev(k_pool, "k_pool", torch.uint8, device)
+    device = k_pool.device
+    _dev(v_pool, "v_pool", torch.uint8, device)
+    _dev(k_scale, "k_scale", torch.float32, device)
+    _dev(v_scale, "v_scale", torch.float32, device)
     if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("FP8 pools must be uint8 [num_blocks, H, 16, D]")
     if k_scale.shape != k_pool.shape[:2] or v_scale.shape != k_scale.shape:
@@ -491,17 +590,18 @@ def attn_paged_append_fp8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_
     """Quantise k_new, v_new [B, H, n_new, D] (bf16) into FP8 pools (uint8
     E4M3 codes [N, H, 16, D] with float32 scales [N, H]), in place."""
     _dev(k_new, "k_new", torch.bfloat16)
-    _dev(v_new, "v_new", torch.bfloat16)
-    nblk, H, bs, D = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    dev = k_new.device
+    _dev(v_new, "v_new", torch.bfloat16, dev)
+    nblk, H, bs, D = _fp8_pools(k_pool, v_pool, k_scale, v_scale, dev)
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
     if k_new.dim() != 4 or v_new.shape != k_new.shape or k_new.shape[1] != H \
             or k_new.shape[3] != D:
         raise ValueError("k_new, v_new must be [B, H, n_new, D] matching the pools")
     B, _, n_new, _ = k_new.shape
     if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_tables must be [B, W] and seq_lens [B]")
-    _check_tables(block_tables, seq_lens, nblk, 0, "attn_paged_append_fp8", stream)
+    _check_append_tables(block_tables, seq_lens, nblk, n_new, "attn_paged_append_fp8", stream)
     st = lib.attn_paged_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                    _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                                    _ptr(seq_lens), B, H, n_new, D, nblk, block_tables.shape[1],
@@ -512,10 +612,12 @@ def attn_paged_append_fp8(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_
 def attn_paged_copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src, dst, *, stream=None):
     """Copy FP8 block src[i] (codes and scales) onto dst[i] in both pools."""
     nblk, H, _, D = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
-    _dev(src, "src", torch.int32)
-    _dev(dst, "dst", torch.int32)
+    _dev(src, "src", torch.int32, k_pool.device)
+    _dev(dst, "dst", torch.int32, k_pool.device)
     if src.dim() != 1 or dst.shape != src.shape:
         raise ValueError("src, dst must be 1-D of one length")
+    if src.numel() > 0:
+        _check_ids(src, dst, nblk, "attn_paged_copy_blocks_fp8", stream)
     st = lib.attn_paged_copy_blocks_fp8(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
                                         _ptr(src), _ptr(dst), src.numel(), nblk, H, D,
                                         _stream(k_pool.device, stream))
@@ -528,9 +630,10 @@ def attn_paged_decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq
     """Attention of q [B, Hq, q_len, D] (bf16) over FP8 pools (uint8 E4M3
     [N, Hkv, 16, D], float32 scales [N, Hkv]); Hkv divides Hq."""
     _dev(q, "q", torch.bfloat16)
-    nblk, Hkv, bs, Dp = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(seq_lens, "seq_lens", torch.int32)
+    dev = q.device
+    nblk, Hkv, bs, Dp = _fp8_pools(k_pool, v_pool, k_scale, v_scale, dev)
+    _dev(block_tables, "block_tables", torch.int32, dev)
+    _dev(seq_lens, "seq_lens", torch.int32, dev)
     if q.dim() != 4:
         raise ValueError("q must be [B, Hq, q_len, D]")
     B, Hq, q_len, D = q.shape
@@ -543,15 +646,13 @@ def attn_paged_decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq
         scale = 1.0 / math.sqrt(D)
     if o is None:
         o = torch.empty_like(q)
-    _dev(o, "o", torch.bfloat16)
+    _dev(o, "o", torch.bfloat16, dev, q.shape)
     if return_lse and lse is None:
-        lse = torch.empty((B, Hq, q_len), device=q.device, dtype=torch.float32)
+        lse = torch.empty((B, Hq, q_len), device=dev, dtype=torch.float32)
     if lse is not None:
-        _dev(lse, "lse", torch.float32)
+        _dev(lse, "lse", torch.float32, dev, (B, Hq, q_len))
     need = attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, width, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need // 4, device=q.device, dtype=torch.float32)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     _check_tables(block_tables, seq_lens, nblk, q_len, "attn_paged_decode_fp8", stream)
     st = lib.attn_paged_decode_fp8(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
                                    _ptr(v_scale), _ptr(block_tables), _ptr(seq_lens), _ptr(o),

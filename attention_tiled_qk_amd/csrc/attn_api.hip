@@ -36,17 +36,22 @@ hipError_t launch_paged_append_fp8(const void*, const void*, void*, void*, float
                                    hipStream_t);
 hipError_t launch_paged_copy_blocks_fp8(void*, void*, float*, float*, const int32_t*,
                                         const int32_t*, int, int, int, hipStream_t);
-hipError_t launch_probe_block_read(const void*, int, const int32_t*, int, uint32_t*, int, int,
-                                   hipStream_t);
 hipError_t launch_check_tables(const int32_t*, const int32_t*, int, int, int, int, int32_t*,
                                hipStream_t);
+hipError_t launch_check_append(const int32_t*, const int32_t*, int, int, int, int, int32_t*,
+                               hipStream_t);
+hipError_t launch_check_ragged(const int32_t*, const int32_t*, int, int, int, int32_t*,
+                               hipStream_t);
+hipError_t launch_check_ids(const int32_t*, const int32_t*, int, int, int32_t*, hipStream_t);
+int prefill_bf16_rows();
+int prefill_f32_rows();
 }  // namespace attn
 
 namespace {
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
-constexpr int kPrefillRowsBf16 = 128;  // query rows per prefill workgroup (bf16)
-constexpr int kPrefillRowsF32 = 8;
+// work-items of a one-dimensional launch (grid x block) must fit 32 bits
+constexpr long long kMaxItems = 0xffffffffLL;
 constexpr int kMaxMergeSplits = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -72,8 +77,8 @@ long long checked_mul(std::initializer_list<long long> xs) {
 // as long as every split keeps at least 4 blocks. Grouped-query waves write
 // `group` partial rows per split, so they take splits of about 64 blocks.
 int auto_splits(int B, int H, int max_blocks, int group) {
-  const int per = group > 1 ? 64 : 32;
-  long long s = (max_blocks + per - 1) / per;
+  const long long per = group > 1 ? 64 : 32;
+  long long s = ((long long)max_blocks + per - 1) / per;
   const long long waves = (long long)B * H;
   long long fill = (2048 + waves - 1) / waves;
   if (fill > max_blocks / 4) fill = max_blocks / 4;
@@ -125,7 +130,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   if (checked_mul({B, H, L, D, 4}) < 0) return ATTN_ERR_OVERFLOW;
   // the bf16 kernel addresses one head's K/V through a 32-bit byte range
   if ((long long)L * D * 2 > 0x7fffffffLL) return ATTN_ERR_OVERFLOW;
-  const int rows = dtype == ATTN_BF16 ? kPrefillRowsBf16 : kPrefillRowsF32;
+  const int rows = dtype == ATTN_BF16 ? attn::prefill_bf16_rows() : attn::prefill_f32_rows();
   if ((long long)B * H * ((L + rows - 1) / rows) > kMaxGrid) return ATTN_ERR_OVERFLOW;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16)
@@ -192,6 +197,8 @@ int paged_decode(const void* q, const void* k_pool, const void* v_pool, const fl
   // one wave 255 us). The workspace size query stays that of the bf16 call,
   // which is never smaller.
   if (k_scale != nullptr && num_splits == 0) S = (S + 3) / 4;
+  // the merge runs one workgroup of D threads per (sequence, head, query) row
+  if (S > 1 && (long long)B * Hq * q_len * D > kMaxItems) return ATTN_ERR_OVERFLOW;
   const size_t need = workspace_for(B, Hq, q_len, D, S);
   float* o_part = nullptr;
   float* lse_part = nullptr;
@@ -237,8 +244,8 @@ int attn_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
   if (checked_mul({num_blocks, H, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
       checked_mul({B, H, q_len, D, 4}) < 0)
     return ATTN_ERR_OVERFLOW;
-  if ((long long)B * H * ((q_len + kPrefillRowsBf16 - 1) / kPrefillRowsBf16) > kMaxGrid)
-    return ATTN_ERR_OVERFLOW;
+  const int rows = attn::prefill_bf16_rows();
+  if ((long long)B * H * ((q_len + rows - 1) / rows) > kMaxGrid) return ATTN_ERR_OVERFLOW;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
     return ATTN_ERR_MISALIGNED;
   if (!aligned4(block_tables) || !aligned4(seq_lens) || (lse && !aligned4(lse)))
@@ -284,8 +291,8 @@ int attn_paged_prefill_gqa(const void* q, const void* k_pool, const void* v_pool
   if (checked_mul({num_blocks, Hkv, 16, D, 2}) < 0 || checked_mul({B, max_blocks_per_seq}) < 0 ||
       checked_mul({total_q, H, D, 4}) < 0)
     return ATTN_ERR_OVERFLOW;
-  if ((long long)B * H * ((max_q_len + kPrefillRowsBf16 - 1) / kPrefillRowsBf16) > kMaxGrid)
-    return ATTN_ERR_OVERFLOW;
+  const int rows = attn::prefill_bf16_rows();
+  if ((long long)B * H * ((max_q_len + rows - 1) / rows) > kMaxGrid) return ATTN_ERR_OVERFLOW;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o))
     return ATTN_ERR_MISALIGNED;
   if (!aligned4(block_tables) || !aligned4(seq_lens) || !aligned4(cu_q_lens) ||
@@ -334,7 +341,8 @@ int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* l
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (S > kMaxMergeSplits) return ATTN_ERR_UNSUPPORTED;
   const long long rows = checked_mul({B, H, q_len});
-  if (rows < 0 || rows > kMaxGrid || checked_mul({rows, S, D, 4}) < 0) return ATTN_ERR_OVERFLOW;
+  if (rows < 0 || rows > kMaxGrid || rows * D > kMaxItems || checked_mul({rows, S, D, 4}) < 0)
+    return ATTN_ERR_OVERFLOW;
   if (!aligned16(o_part) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
   if (!aligned4(lse_part) || (lse && !aligned4(lse))) return ATTN_ERR_MISALIGNED;
   return hip_status(attn::launch_lse_merge(o_part, lse_part, o, lse, rows, S, D,
@@ -372,21 +380,33 @@ int attn_paged_check_tables(const int32_t* block_tables, const int32_t* seq_lens
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
-int attn_probe_block_read(const void* buf, int num_blocks, int block_bytes, const int32_t* order,
-                          int n_reads, uint32_t* sink, int n_waves, int nontemporal,
-                          void* stream) {
-  if (!buf || !order || !sink) return ATTN_ERR_NULL_PTR;
-  if (num_blocks <= 0 || n_reads <= 0) return ATTN_ERR_BAD_SHAPE;
-  if (block_bytes != 1024 && block_bytes != 2048 && block_bytes != 4096 && block_bytes != 8192 &&
-      block_bytes != 16384)
-    return ATTN_ERR_UNSUPPORTED;
-  if (n_waves < 4 || n_waves > (1 << 22) || n_waves % 4 != 0) return ATTN_ERR_BAD_SHAPE;
-  if (nontemporal != 0 && nontemporal != 1) return ATTN_ERR_BAD_SHAPE;
-  if (!aligned16(buf)) return ATTN_ERR_MISALIGNED;
-  if (!aligned4(order) || !aligned4(sink)) return ATTN_ERR_MISALIGNED;
-  return hip_status(attn::launch_probe_block_read(buf, block_bytes, order, n_reads, sink, n_waves,
-                                                  nontemporal,
-                                                  reinterpret_cast<hipStream_t>(stream)));
+int attn_paged_check_append(const int32_t* block_tables, const int32_t* seq_lens, int B, int n_new,
+                            int num_blocks, int max_blocks_per_seq, int32_t* bad, void* stream) {
+  if (!block_tables || !seq_lens || !bad) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || n_new <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (checked_mul({B, max_blocks_per_seq}) < 0) return ATTN_ERR_OVERFLOW;
+  if (!aligned4(block_tables) || !aligned4(seq_lens) || !aligned4(bad)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_check_append(block_tables, seq_lens, B, n_new, num_blocks,
+                                              max_blocks_per_seq, bad,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_check_ragged(const int32_t* cu_q_lens, const int32_t* seq_lens, int B, int total_q,
+                            int max_q_len, int32_t* bad, void* stream) {
+  if (!cu_q_lens || !seq_lens || !bad) return ATTN_ERR_NULL_PTR;
+  if (B <= 0 || total_q <= 0 || max_q_len <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (!aligned4(cu_q_lens) || !aligned4(seq_lens) || !aligned4(bad)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_check_ragged(cu_q_lens, seq_lens, B, total_q, max_q_len, bad,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attn_paged_check_ids(const int32_t* src, const int32_t* dst, int n, int num_blocks,
+                         int32_t* bad, void* stream) {
+  if (!src || !dst || !bad) return ATTN_ERR_NULL_PTR;
+  if (n <= 0 || num_blocks <= 0) return ATTN_ERR_BAD_SHAPE;
+  if (!aligned4(src) || !aligned4(dst) || !aligned4(bad)) return ATTN_ERR_MISALIGNED;
+  return hip_status(attn::launch_check_ids(src, dst, n, num_blocks, bad,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 int attn_paged_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,

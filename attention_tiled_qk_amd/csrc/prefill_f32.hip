@@ -139,6 +139,9 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
   return hipGetLastError();
 }
 
+// Query rows per workgroup of the float32 prefill kernel (sizes its grid).
+int prefill_f32_rows() { return R_WAVES; }
+
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int H, int L, int D, int causal, float scale,
                               hipStream_t stream) {

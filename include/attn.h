@@ -37,7 +37,8 @@
  *     error the call returns a negative ATTN_ERR_* code and enqueues nothing.
  *     Device-side contents are trusted: block ids outside [0, num_blocks) or
  *     seq_lens above max_blocks_per_seq * 16 are undefined behaviour;
- *     attn_paged_check_tables counts such entries on the device.
+ *     attn_paged_check_tables, _check_append, _check_ragged and _check_ids
+ *     count such entries on the device.
  *   - Calls are stateless and re-entrant; calls on different streams may run
  *     concurrently if their output buffers do not overlap.
  */
@@ -95,11 +96,16 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * attn_paged_workspace_bytes -- size of the float32 scratch that
- * attn_paged_decode needs for `num_splits` split-KV partials: the normalised
- * partial outputs [B, H, q_len, S, D] and their lse [B, H, q_len, S].
- * num_splits = 0 asks for the split count the library would choose itself for
- * the given max_blocks_per_seq. Returns 0 when one split suffices (no
- * workspace needed) and also for invalid arguments.
+ * attn_paged_decode needs for `num_splits` split-KV partials ([P3]
+ * FlashDecoding item: each split of the key range is attended on its own and
+ * leaves a partial output and its log-sum-exp for the reduction): the
+ * normalised partial outputs [B, H, q_len, S, D] and their lse
+ * [B, H, q_len, S], 4 * B * H * q_len * S * (D + 1) bytes.
+ * num_splits = 0 asks for the split count the library would choose itself,
+ * which depends on the table width, so max_blocks_per_seq is an argument here
+ * as well (it must be the max_blocks_per_seq of the decode call). Returns 0
+ * when one split suffices (no workspace needed) and also for invalid
+ * arguments.
  */
 size_t attn_paged_workspace_bytes(int B, int H, int q_len, int D, int max_blocks_per_seq,
                                   int num_splits);
@@ -318,6 +324,43 @@ int attn_paged_check_tables(const int32_t* block_tables, const int32_t* seq_lens
                             void* stream);
 
 /*
+ * attn_paged_check_append -- attn_paged_check_tables for the append calls,
+ * which read different entries: for each sequence, the entries covering its
+ * n_new newest positions (those >= 0). Those must be -1 (the append places
+ * nothing there) or inside [0, num_blocks).
+ *   bad : 2 int32 device words, overwritten, each saturating at INT32_MAX:
+ *         bad[0] = sequences with seq_lens[b] < 0 or > max_blocks_per_seq * 16;
+ *         bad[1] = entries the append writes through that are < -1 or
+ *                  >= num_blocks.
+ * One workgroup on stream. Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_check_append(const int32_t* block_tables, const int32_t* seq_lens, int B, int n_new,
+                            int num_blocks, int max_blocks_per_seq, int32_t* bad, void* stream);
+
+/*
+ * attn_paged_check_ragged -- checks the packed query offsets of a ragged
+ * prefill call (attn_paged_prefill_varlen / _gqa), which trusts them:
+ *   cu_q_lens : [B + 1] int32 device.  seq_lens : [B] int32 device.
+ *   bad       : 2 int32 device words, overwritten, each saturating:
+ *               bad[0] = offset errors: cu_q_lens[0] != 0, cu_q_lens[B] !=
+ *                        total_q, and each decreasing step;
+ *               bad[1] = sequences whose query count exceeds max_q_len or
+ *                        their seq_lens[b].
+ * One workgroup on stream. Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_check_ragged(const int32_t* cu_q_lens, const int32_t* seq_lens, int B, int total_q,
+                            int max_q_len, int32_t* bad, void* stream);
+
+/*
+ * attn_paged_check_ids -- checks the block-id lists of a copy call
+ * (attn_paged_copy_blocks / _fp8): bad[0] counts entries of src and bad[1]
+ * entries of dst outside [0, num_blocks) (n ids each, int32 device arrays).
+ * One workgroup on stream. Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_paged_check_ids(const int32_t* src, const int32_t* dst, int n, int num_blocks,
+                         int32_t* bad, void* stream);
+
+/*
  * attn_paged_append -- write n_new new tokens of K and V per sequence into the
  * paged pools ([P1] §3.2 layout; [P3] Continuous Batching + PagedAttention:
  * the cache grows block by block). Token t of sequence b has position
@@ -477,34 +520,6 @@ int attn_paged_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
                           int q_len, int D, int num_blocks, int max_blocks_per_seq,
                           int block_size, int causal, float scale, int num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
-
-/*
- * attn_probe_block_read -- diagnostic: read whole blocks of a device buffer in
- * a given order and compute nothing else, to measure the read bandwidth HBM
- * sustains for an access pattern: the ceiling of the memory-bound paged
- * kernels, in the sense of the roofline of [P4] (scattered 2 and 4 KiB cache
- * slabs sustain less than streaming reads).
- *
- *   buf         : num_blocks * block_bytes bytes of device memory, 16-byte
- *                 aligned.
- *   block_bytes : 1024, 2048, 4096, 8192 or 16384.
- *   order       : [n_reads] int32 device: the block ids to read, each in
- *                 [0, num_blocks) (not checked on the device: an id outside is
- *                 undefined behaviour, as for block tables).
- *   sink        : [n_waves * 64] uint32 device, written: lane l of wave w
- *                 stores the XOR of the 32-bit words it read, so the XOR of
- *                 all sink words equals the XOR of every word of every block
- *                 read (each entry of order counted once).
- *   n_waves     : waves launched, a multiple of 4 in [4, 2^22]; wave w reads
- *                 order[w], order[w + n_waves], ..., two blocks at a time, 16
- *                 bytes per lane per load.
- *   nontemporal : 0 = default cache policy, 1 = nontemporal loads (the policy
- *                 the paged attention kernels use for the cache).
- * Returns ATTN_OK or a negative ATTN_ERR_* code.
- */
-int attn_probe_block_read(const void* buf, int num_blocks, int block_bytes, const int32_t* order,
-                          int n_reads, uint32_t* sink, int n_waves, int nontemporal,
-                          void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_string(int status);

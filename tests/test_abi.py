@@ -204,26 +204,72 @@ def test_check_tables_rejects_bad_arguments(api):
     assert call(bad=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
 
 
-def test_probe_rejects_bad_arguments(api):
-    c = header_constants()
-    L = api.lib
+def test_probe_is_a_library_of_its_own(api):
+    """The benchmark's bandwidth probe is not part of the attention library."""
+    assert not hasattr(api.lib, "attn_probe_block_read")
+    assert "probe" not in " ".join(declared_functions())
+
+
+def test_probe_rejects_bad_arguments():
+    import probe
+    L = probe.lib()
 
     def call(buf=FAKE, nb=64, bb=4096, order=FAKE, n=64, sink=FAKE, waves=8, nt=0):
-        return L.attn_probe_block_read(buf, nb, bb, order, n, sink, waves, nt, None)
+        return L.probe_block_read(buf, nb, bb, order, n, sink, waves, nt, None)
 
-    assert call(buf=None) == c["ATTN_ERR_NULL_PTR"]
-    assert call(order=None) == c["ATTN_ERR_NULL_PTR"]
-    assert call(sink=None) == c["ATTN_ERR_NULL_PTR"]
-    assert call(nb=0) == c["ATTN_ERR_BAD_SHAPE"]
-    assert call(n=0) == c["ATTN_ERR_BAD_SHAPE"]
-    assert call(bb=3072) == c["ATTN_ERR_UNSUPPORTED"]
-    assert call(bb=32768) == c["ATTN_ERR_UNSUPPORTED"]
-    assert call(waves=6) == c["ATTN_ERR_BAD_SHAPE"]
-    assert call(waves=0) == c["ATTN_ERR_BAD_SHAPE"]
-    assert call(waves=1 << 23) == c["ATTN_ERR_BAD_SHAPE"]
-    assert call(nt=2) == c["ATTN_ERR_BAD_SHAPE"]
-    assert call(buf=FAKE_ODD) == c["ATTN_ERR_MISALIGNED"]
-    assert call(order=ctypes.c_void_p((1 << 20) + 2)) == c["ATTN_ERR_MISALIGNED"]
+    assert call(buf=None) == -1
+    assert call(order=None) == -1
+    assert call(sink=None) == -1
+    assert call(nb=0) == -2
+    assert call(n=0) == -2
+    assert call(bb=3072) == -4
+    assert call(bb=32768) == -4
+    assert call(waves=6) == -2
+    assert call(waves=0) == -2
+    assert call(waves=1 << 23) == -2
+    assert call(nt=2) == -2
+    assert call(buf=FAKE_ODD) == -5
+    assert call(order=ctypes.c_void_p((1 << 20) + 2)) == -5
+
+
+def test_new_checks_reject_bad_arguments(api):
+    c = header_constants()
+    L = api.lib
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    # append tables
+    assert L.attn_paged_check_append(None, FAKE, 2, 3, 64, 8, FAKE, None) == c["ATTN_ERR_NULL_PTR"]
+    assert L.attn_paged_check_append(FAKE, FAKE, 0, 3, 64, 8, FAKE, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_paged_check_append(FAKE, FAKE, 2, 0, 64, 8, FAKE, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_paged_check_append(FAKE, FAKE, 2, 3, 64, 8, odd, None) == c["ATTN_ERR_MISALIGNED"]
+    # ragged offsets
+    assert L.attn_paged_check_ragged(None, FAKE, 2, 40, 30, FAKE, None) == c["ATTN_ERR_NULL_PTR"]
+    assert L.attn_paged_check_ragged(FAKE, FAKE, 2, 0, 30, FAKE, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_paged_check_ragged(FAKE, FAKE, 2, 40, 0, FAKE, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_paged_check_ragged(odd, FAKE, 2, 40, 30, FAKE, None) == c["ATTN_ERR_MISALIGNED"]
+    # id lists
+    assert L.attn_paged_check_ids(FAKE, None, 4, 64, FAKE, None) == c["ATTN_ERR_NULL_PTR"]
+    assert L.attn_paged_check_ids(FAKE, FAKE, 0, 64, FAKE, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_paged_check_ids(FAKE, FAKE, 4, 0, FAKE, None) == c["ATTN_ERR_BAD_SHAPE"]
+    assert L.attn_paged_check_ids(FAKE, odd, 4, 64, FAKE, None) == c["ATTN_ERR_MISALIGNED"]
+
+
+def test_launch_size_limits(api):
+    """Grids that the kernels could not be launched with are refused before
+    anything is enqueued (a float32 prefill workgroup holds 4 query rows; the
+    merge runs D threads per row, and a launch's work-items fit 32 bits)."""
+    c = header_constants()
+    L = api.lib
+    # float32 prefill: 2^29 heads x 16 rows / 4 rows per workgroup = 2^31
+    # workgroups, one past the limit (8 rows per workgroup would have passed)
+    assert L.attn_prefill(FAKE, FAKE, FAKE, FAKE, None, 1 << 29, 1, 16, 64, 1, 0.1, 0, None) == \
+        c["ATTN_ERR_OVERFLOW"]
+    # merge: 2^25 rows x 128 threads = 2^32 work-items
+    assert L.attn_lse_merge(FAKE, FAKE, FAKE, None, 1 << 25, 1, 1, 2, 128, 1, None) == \
+        c["ATTN_ERR_OVERFLOW"]
+    # paged decode with splits: the merge of 65535 x 65535 rows does not fit
+    need = L.attn_paged_workspace_bytes(65535, 65535, 1, 128, 8, 2)
+    assert L.attn_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 65535, 65535, 1, 128, 10,
+                               8, 16, 1, 0.1, 2, FAKE, need, 1, None) == c["ATTN_ERR_OVERFLOW"]
 
 
 def test_binding_refuses_cpu_tensors(api):
