@@ -8,6 +8,7 @@ step of the computation runs in the HIP kernels; there is no fallback path.
 If the shared library has not been built, importing this package raises.
 """
 
+import contextlib
 import ctypes
 import math
 import os
@@ -18,7 +19,8 @@ from .build import LIB_PATH
 
 __all__ = [
     "AttnError", "attn_prefill", "attn_paged_decode", "attn_paged_workspace_bytes",
-    "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_prefill",
+    "attn_paged_decode_gqa", "attn_paged_gqa_workspace_bytes", "attn_paged_decode_noalloc",
+    "ATTN_NOALLOC_SCRATCH_BYTES", "attn_paged_prefill",
     "attn_paged_prefill_varlen", "attn_paged_prefill_gqa",
     "attn_lse_merge", "attn_paged_gather", "attn_paged_append", "attn_paged_copy_blocks",
     "KVCacheAllocator", "attn_paged_append_fp8", "attn_paged_copy_blocks_fp8",
@@ -30,6 +32,8 @@ __all__ = [
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
+# per-GPU scratch of attn_paged_decode_noalloc (ATTN_NOALLOC_SCRATCH_BYTES in attn.h)
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -52,6 +56,9 @@ lib.attn_paged_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i
 lib.attn_paged_decode.restype = _i
 lib.attn_paged_gqa_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 lib.attn_paged_gqa_workspace_bytes.restype = _sz
+lib.attn_paged_decode_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                          _i, _i, _f, _i, _i, _p]
+lib.attn_paged_decode_noalloc.restype = _i
 lib.attn_paged_decode_gqa.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                                       _i, _f, _i, _p, _sz, _i, _p]
 lib.attn_paged_decode_gqa.restype = _i
@@ -263,17 +270,10 @@ def attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, max_blocks_per_seq, num
                                                   num_splits))
 
 
-def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True, scale=None,
-                      num_splits=0, o=None, lse=None, return_lse=False, workspace=None,
-                      stream=None):
-    """Attention of q [B, H, q_len, D] (bf16) over a paged K/V cache.
-
-    k_pool, v_pool [num_blocks, H, 16, D] bf16; block_tables [B, W] int32;
-    seq_lens [B] int32 (key counts including the q_len new tokens). A float32
-    workspace is allocated here when the split count needs one and none is given.
-    When the pools hold fewer heads than q (a divisor of them), the call goes to
-    attn_paged_decode_gqa (grouped-query attention).
-    """
+def _paged_decode_args(q, k_pool, v_pool, block_tables, seq_lens, scale, o, lse, return_lse):
+    """Checks of the paged decode arguments; allocates o (and lse when asked
+    for) if not given. Returns (B, Hq, Hkv, q_len, D, num_blocks, block_size,
+    table width, scale, o, lse)."""
     _dev(q, "q", torch.bfloat16)
     dev = q.device
     _dev(k_pool, "k_pool", torch.bfloat16, dev)
@@ -298,6 +298,23 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
         lse = torch.empty((B, Hq, q_len), device=dev, dtype=torch.float32)
     if lse is not None:
         _dev(lse, "lse", torch.float32, dev, (B, Hq, q_len))
+    return B, Hq, Hkv, q_len, D, nblk, bs, width, scale, o, lse
+
+
+def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True, scale=None,
+                      num_splits=0, o=None, lse=None, return_lse=False, workspace=None,
+                      stream=None):
+    """Attention of q [B, H, q_len, D] (bf16) over a paged K/V cache.
+
+    k_pool, v_pool [num_blocks, H, 16, D] bf16; block_tables [B, W] int32;
+    seq_lens [B] int32 (key counts including the q_len new tokens). A float32
+    workspace is allocated here when the split count needs one and none is given.
+    When the pools hold fewer heads than q (a divisor of them), the call goes to
+    attn_paged_decode_gqa (grouped-query attention).
+    """
+    B, Hq, Hkv, q_len, D, nblk, bs, width, scale, o, lse = _paged_decode_args(
+        q, k_pool, v_pool, block_tables, seq_lens, scale, o, lse, return_lse)
+    dev = q.device
     need = attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, width, num_splits)
     workspace, ws_bytes = _workspace(workspace, need, dev)
     common = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), _ptr(o),
@@ -311,6 +328,29 @@ def attn_paged_decode(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
     else:
         st = lib.attn_paged_decode_gqa(*common, Hq, Hkv, *tail)
         _check(st, "attn_paged_decode_gqa")
+    return (o, lse) if (return_lse or lse is not None) else o
+
+
+def attn_paged_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, *, causal=True,
+                              scale=None, num_splits=0, o=None, lse=None, return_lse=False,
+                              stream=None):
+    """attn_paged_decode (multi-head or grouped-query) whose split-KV partials
+    live in the library's per-GPU static scratch: the library call allocates
+    no device memory. Pass o (and lse) to keep this wrapper from allocating
+    them. Calls on one GPU that may overlap in time race on the scratch.
+    Raises AttnError (ATTN_ERR_SCRATCH) when the partials exceed
+    ATTN_NOALLOC_SCRATCH_BYTES."""
+    B, Hq, Hkv, q_len, D, nblk, bs, width, scale, o, lse = _paged_decode_args(
+        q, k_pool, v_pool, block_tables, seq_lens, scale, o, lse, return_lse)
+    _check_tables(block_tables, seq_lens, nblk, q_len, "attn_paged_decode_noalloc", stream)
+    # the first call on a GPU looks its scratch up with that GPU current
+    ctx = torch.cuda.device(q.device) if q.device.type == "cuda" else contextlib.nullcontext()
+    with ctx:
+        st = lib.attn_paged_decode_noalloc(
+            _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), _ptr(o),
+            _ptr(lse), B, Hq, Hkv, q_len, D, nblk, width, bs, int(bool(causal)), float(scale),
+            int(num_splits), ATTN_BF16, _stream(q.device, stream))
+    _check(st, "attn_paged_decode_noalloc")
     return (o, lse) if (return_lse or lse is not None) else o
 
 

@@ -1,10 +1,13 @@
 // Host side of the C ABI declared in include/attn.h: argument validation, the
 // split-count choice for paged decode, and kernel launches on the caller's
 // stream. Everything is checked before anything is enqueued; the library owns
-// no memory and keeps no state besides per-kernel launch attributes.
+// no memory besides the per-GPU scratch array of the no-allocation decode
+// entry point, and keeps no state besides per-kernel launch attributes and
+// that array's device addresses.
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -113,6 +116,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_OVERFLOW: return "sizes overflow the kernels' indexing";
     case ATTN_ERR_HIP: return "kernel launch failed";
     case ATTN_ERR_NO_BLOCKS: return "the block pool has too few free blocks";
+    case ATTN_ERR_SCRATCH: return "split-KV partials exceed the static scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -331,6 +335,59 @@ int attn_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                       Hkv, q_len, D,
                       num_blocks, max_blocks_per_seq, block_size, causal, scale, num_splits,
                       workspace, workspace_bytes, dtype, stream);
+}
+
+}  // extern "C"
+
+// Split-KV partials of attn_paged_decode_noalloc. Each GPU the code object is
+// loaded onto holds its own copy until the process ends. Host code never uses
+// this name as an address (on the host it only identifies the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_addr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on the first call
+// on that device, which is current then; the result, or the failure, is kept).
+int device_scratch(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_addr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_addr[dev] == nullptr) return ATTN_ERR_HIP;
+  *addr = g_scratch_addr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int q_len, int D,
+                              int num_blocks, int max_blocks_per_seq, int block_size, int causal,
+                              float scale, int num_splits, int dtype, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !o) return ATTN_ERR_NULL_PTR;
+  // 0 for invalid arguments too: paged_decode reports those
+  const size_t need = paged_workspace(B, Hq, Hkv, q_len, D, max_blocks_per_seq, num_splits);
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = device_scratch(&ws);
+    if (st != ATTN_OK) return st;
+  }
+  return paged_decode(q, k_pool, v_pool, nullptr, nullptr, block_tables, seq_lens, o, lse, B, Hq,
+                      Hkv, q_len, D, num_blocks, max_blocks_per_seq, block_size, causal, scale,
+                      num_splits, ws, need, dtype, stream);
 }
 
 int attn_lse_merge(const float* o_part, const float* lse_part, void* o, float* lse, int B, int H,

@@ -66,7 +66,8 @@ enum attn_status {
   ATTN_ERR_WORKSPACE = -6,   /* workspace missing or smaller than attn_paged_workspace_bytes() */
   ATTN_ERR_OVERFLOW = -7,    /* an element count does not fit the kernels' 32/64-bit indexing */
   ATTN_ERR_HIP = -8,         /* the kernel launch itself failed (hipGetLastError) */
-  ATTN_ERR_NO_BLOCKS = -9    /* the block allocator has too few free blocks */
+  ATTN_ERR_NO_BLOCKS = -9,   /* the block allocator has too few free blocks */
+  ATTN_ERR_SCRATCH = -10     /* split-KV partials larger than ATTN_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Largest query count per sequence accepted by attn_paged_decode. */
@@ -252,6 +253,37 @@ int attn_paged_decode_gqa(const void* q, const void* k_pool, const void* v_pool,
                           int max_blocks_per_seq, int block_size, int causal, float scale,
                           int num_splits, void* workspace, size_t workspace_bytes, int dtype,
                           void* stream);
+
+/* Size of the device scratch that attn_paged_decode_noalloc keeps per GPU. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * attn_paged_decode_noalloc -- attn_paged_decode_gqa for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split-KV partials go to a scratch
+ * array of ATTN_NOALLOC_SCRATCH_BYTES that the library's code object reserves
+ * on each GPU it is loaded onto, held until the process ends. The call itself
+ * allocates nothing; its first call on a device looks the array's device
+ * address up (hipGetSymbolAddress) for that device.
+ *
+ *   Arguments: those of attn_paged_decode_gqa without the workspace (Hkv == Hq
+ *   for plain multi-head attention); the call runs on the current device, to
+ *   which `stream` must belong. Outputs are identical to attn_paged_decode_gqa
+ *   with the same num_splits.
+ *   Returns ATTN_ERR_SCRATCH (before anything is enqueued) when the partials,
+ *   attn_paged_gqa_workspace_bytes(B, Hq, Hkv, q_len, D, max_blocks_per_seq,
+ *   num_splits) bytes, exceed ATTN_NOALLOC_SCRATCH_BYTES; ATTN_ERR_HIP when
+ *   the device address cannot be obtained; otherwise as attn_paged_decode_gqa.
+ *   All calls on one GPU share its scratch: calls that may overlap in time on
+ *   one GPU (other streams, other host threads) race on it and must be
+ *   serialised by the caller. Every call writes the partials it reads, so
+ *   what an earlier call left there does not matter.
+ */
+int attn_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                              float* lse, int B, int Hq, int Hkv, int q_len, int D,
+                              int num_blocks, int max_blocks_per_seq, int block_size, int causal,
+                              float scale, int num_splits, int dtype, void* stream);
 
 /*
  * attn_paged_gqa_workspace_bytes -- split-KV scratch size for

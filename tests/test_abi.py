@@ -356,3 +356,51 @@ def test_paged_prefill_gqa_rejects_bad_arguments(api):
 def test_binding_exports_what_it_lists(api):
     for name in api.__all__:
         assert hasattr(api, name), name
+
+
+def test_noalloc_decode_refuses_partials_beyond_its_scratch(api):
+    """attn_paged_decode_noalloc refuses, before anything touches a device,
+    a call whose split-KV partials exceed the static scratch, and matches the
+    binding's constant for its size."""
+    c = header_constants()
+    L = api.lib
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == api.ATTN_NOALLOC_SCRATCH_BYTES
+    limit = api.ATTN_NOALLOC_SCRATCH_BYTES
+
+    def call(B, Hq, Hkv, q_len, W, S, q=FAKE, o=FAKE):
+        return L.attn_paged_decode_noalloc(q, FAKE, FAKE, FAKE, FAKE, o, None, B, Hq, Hkv,
+                                           q_len, 128, 64, W, 16, 1, 0.1, S, 1, None)
+
+    assert call(64, 40, 40, 1, 256, 8, q=None) == c["ATTN_ERR_NULL_PTR"]
+    # 64 sequences x 40 heads x 16 queries x 64 splits x 129 floats: 676 MB
+    big = L.attn_paged_gqa_workspace_bytes(64, 40, 40, 16, 128, 4096, 64)
+    assert big > limit
+    assert call(64, 40, 40, 16, 4096, 64) == c["ATTN_ERR_SCRATCH"]
+    # grouped-query: 8 query heads per KV head, q_len 2, 64 splits
+    assert L.attn_paged_gqa_workspace_bytes(512, 64, 8, 2, 128, 4096, 64) > limit
+    assert call(512, 64, 8, 2, 4096, 64) == c["ATTN_ERR_SCRATCH"]
+    # the boundary: the largest split count whose partials still fit is not
+    # refused for size; it fails later, at the device lookup (no GPU) or on
+    # the misaligned output pointer, so that nothing is ever launched
+    B, H, q_len = 64, 40, 4
+    per_split = L.attn_paged_gqa_workspace_bytes(B, H, H, q_len, 128, 4096, 2) // 2
+    s_fit = limit // per_split
+    assert 2 <= s_fit < 64
+    assert call(B, H, H, q_len, 4096, s_fit + 1) == c["ATTN_ERR_SCRATCH"]
+    assert call(B, H, H, q_len, 4096, s_fit, o=FAKE_ODD) in (c["ATTN_ERR_HIP"],
+                                                             c["ATTN_ERR_MISALIGNED"])
+
+
+def test_library_imports_no_device_allocator(api):
+    """The library never allocates device or host memory through HIP: none of
+    HIP's allocation, free or memset routines is among its imports (the static
+    scratch of attn_paged_decode_noalloc comes with the code object)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    hip = sorted({ln.split()[-1].split("@")[0] for ln in out.splitlines() if "hip" in ln})
+    assert "hipGetSymbolAddress" in hip
+    bad = [n for n in hip if re.search(r"Malloc|Free|Alloc|Memset|MemPool|HostRegister", n)]
+    assert not bad, bad
