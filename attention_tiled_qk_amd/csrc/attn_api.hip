@@ -78,12 +78,16 @@ long long checked_mul(std::initializer_list<long long> xs) {
 // that waves carry similar amounts of work whatever the length mix, raised
 // towards enough (split, head, sequence) waves to cover the chip several times
 // as long as every split keeps at least 4 blocks. Grouped-query waves write
-// `group` partial rows per split, so they take splits of about 64 blocks.
+// `group` partial rows per split and serve `group` heads from one read, so
+// they take splits of about 128 blocks and half the covering target; with
+// such long splits the kernel runs the longest sequences first, which evens
+// the end of the launch (64 sequences, 8 KV heads, group 8, 128 to 4096
+// keys: 2 splits longest-first 95 us, 4 splits in batch order 109 us).
 int auto_splits(int B, int H, int max_blocks, int group) {
-  const long long per = group > 1 ? 64 : 32;
+  const long long per = group > 1 ? 128 : 32;
   long long s = ((long long)max_blocks + per - 1) / per;
   const long long waves = (long long)B * H;
-  long long fill = (2048 + waves - 1) / waves;
+  long long fill = ((group > 1 ? 1024 : 2048) + waves - 1) / waves;
   if (fill > max_blocks / 4) fill = max_blocks / 4;
   if (s < fill) s = fill;
   if (s < 1) s = 1;
@@ -195,12 +199,13 @@ int paged_decode(const void* q, const void* k_pool, const void* v_pool, const fl
   int S = splits_for(B, Hkv, group, max_blocks_per_seq, num_splits);
   // The fp8 kernel runs four waves per (split, head, sequence), merged in LDS
   // (it holds three waves per SIMD, so a workgroup of four does not hold a CU
-  // idle behind its slowest wave): a quarter of the automatic split count gives
-  // its waves the same length with a quarter of the partials (64 sequences x
-  // 40 heads of 128 to 4096 keys: 2 splits of 4 waves take 247 us, 8 splits of
-  // one wave 255 us). The workspace size query stays that of the bf16 call,
-  // which is never smaller.
-  if (k_scale != nullptr && num_splits == 0) S = (S + 3) / 4;
+  // idle behind its slowest wave), and reads half the bytes per block: an
+  // eighth of the automatic split count keeps its items long enough for the
+  // longest-first order (64 sequences x 40 heads of 128 to 4096 keys: 1 split
+  // longest-first 217 us, 2 splits 227 us, 2 splits in batch order 232 us).
+  // The workspace size query stays that of the bf16 call, which is never
+  // smaller.
+  if (k_scale != nullptr && num_splits == 0) S = (S + 7) / 8;
   // the merge runs one workgroup of D threads per (sequence, head, query) row
   if (S > 1 && (long long)B * Hq * q_len * D > kMaxItems) return ATTN_ERR_OVERFLOW;
   const size_t need = workspace_for(B, Hq, q_len, D, S);

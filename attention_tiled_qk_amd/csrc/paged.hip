@@ -64,7 +64,7 @@ void paged_attn_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o_part,
     float* __restrict__ lse_part, int H, int group, int q_len, int max_blocks, int num_splits,
-    int causal, float scale) {
+    int causal, float scale, int longest_first) {
   constexpr int DC = D / 32;            // 32-wide chunks of the QK^T contraction
   constexpr int DB = D / 16;            // 16-wide output blocks
   constexpr int PV = D * 2 + 64;        // LDS row pitch of a V slab (bytes)
@@ -87,7 +87,24 @@ void paged_attn_kernel(
   const int g = lane >> 4;
   const int split = blockIdx.x;
   const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // Longest sequences first (when the host asks for it): workgroups are
+  // dispatched in linear-id order (split fastest, sequence slowest), so the z
+  // index is taken as a rank and mapped to the sequence of that rank by length
+  // (ties by index). The launch then ends on the shortest items instead of on
+  // whichever long sequences come last in the batch. One lane holds one
+  // length, so this takes batches of up to 64 sequences.
+  int b = blockIdx.z;
+  if (longest_first && gridDim.z <= 64) {
+    const int nseq = gridDim.z;
+    const int len = lane < nseq ? seq_lens[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < nseq; ++j) {
+      const int lj = __builtin_amdgcn_readlane(len, j);
+      rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < nseq && rank == (int)blockIdx.z);
+    if (hit != 0) b = __builtin_ctzll(hit);
+  }
 
   const int seq_len = seq_lens[b];
   const int nb = (seq_len + 15) >> 4;
@@ -564,6 +581,7 @@ struct PagedArgs {
   float* lse_part;
   int H, group, q_len, max_blocks, num_splits, causal;
   float scale;
+  int longest_first;
 };
 
 template <int D, int WPS, bool F8>
@@ -571,7 +589,7 @@ static void launch_paged_variant(dim3 grid, hipStream_t stream, const PagedArgs&
   hipLaunchKernelGGL((paged_attn_kernel<D, WPS, F8>), grid, dim3(64 * WPS), 0, stream,
                      (const bf16*)a.q, a.k_pool, a.v_pool, a.k_scale, a.v_scale, a.block_tables,
                      a.seq_lens, (bf16*)a.o, a.lse, a.o_part, a.lse_part, a.H, a.group, a.q_len,
-                     a.max_blocks, a.num_splits, a.causal, a.scale);
+                     a.max_blocks, a.num_splits, a.causal, a.scale, a.longest_first);
 }
 
 template <bool F8>
@@ -599,11 +617,16 @@ hipError_t launch_paged_attn(const void* q, const void* k_pool, const void* v_po
   dim3 grid(num_splits, H, B);
   // With few (split, head, sequence) items the resident waves would leave part
   // of the chip idle in the last round; give each item two waves instead. The
-  // fp8 variant always runs four waves per item (its host side takes a
-  // quarter of the splits).
+  // fp8 variant always runs four waves per item (its host side takes an
+  // eighth of the automatic splits).
   const int wps = k_scale != nullptr ? 4 : (long long)num_splits * H * B < 4096 ? 2 : 1;
+  // Longest-first order pays when splits are long (at least 64 blocks on the
+  // widest table): it removes the tail of long items that start late. With
+  // short splits it gathers the latency-bound items of short sequences at the
+  // end of the launch, where they no longer overlap long streams, and is off.
+  const int longest_first = B <= 64 && (max_blocks + num_splits - 1) / num_splits >= 64 ? 1 : 0;
   const PagedArgs a{q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, o, lse, o_part,
-                    lse_part, H, group, q_len, max_blocks, num_splits, causal, scale};
+                    lse_part, H, group, q_len, max_blocks, num_splits, causal, scale, longest_first};
   if (k_scale != nullptr) launch_paged_dispatch<true>(D, wps, grid, stream, a);
   else launch_paged_dispatch<false>(D, wps, grid, stream, a);
   return hipGetLastError();

@@ -302,6 +302,47 @@ def test_paged_gqa(api, group, q_len, splits):
     assert e <= TOL_BF16 and lse_err(lse, ref_lse) <= TOL_LSE
 
 
+def _reorder(inp, order):
+    """The same sequences in another batch order (same pools and blocks)."""
+    idx = torch.tensor(order)
+    return PagedInputs(inp.q[idx].contiguous(), inp.k_pool, inp.v_pool,
+                       inp.block_tables[idx].contiguous(), inp.seq_lens[idx].contiguous())
+
+
+# Batches with tied lengths, at and past the 64 sequences that the kernel's
+# longest-first order takes (one length per lane), with long splits (the order
+# is used) and short ones (batch order).
+LPT_CASES = [
+    ((300, 1000, 17, 1000, 300, 5, 1000, 64), 1, 2, 1),
+    (tuple(16 + (i * 37) % 1100 // 50 * 50 for i in range(64)), 2, 1, 1),
+    (tuple(16 + (i * 37) % 1100 // 50 * 50 for i in range(65)), 1, 1, 1),
+    ((40, 900, 900, 40, 2000, 41), 3, 2, 2),
+]
+
+
+@pytest.mark.parametrize("lens,q_len,hkv,splits", LPT_CASES)
+def test_paged_longest_first_order(api, lens, q_len, hkv, splits):
+    """Each sequence's output does not depend on where it stands in the batch
+    (the kernel maps launch positions to sequences by length rank), and it
+    matches the oracle."""
+    say(f"longest-first: B={len(lens)} q_len={q_len} hkv={hkv} splits={splits}")
+    group = 2
+    inp = _gqa_inputs(lens, q_len, hkv, group, seed=len(lens) + 7)
+    scale = 1.0 / math.sqrt(128)
+    o1, l1 = _run_paged(api, inp, splits)
+    order = list(range(len(lens)))[::-1]
+    order = order[1::2] + order[0::2]
+    o2, l2 = _run_paged(api, _reorder(inp, order), splits)
+    inv = torch.empty(len(order), dtype=torch.long)
+    inv[torch.tensor(order)] = torch.arange(len(order))
+    assert torch.equal(o1, o2[inv.cuda()]) and torch.equal(l1, l2[inv.cuda()])
+    ref_o, ref_lse = oracle.paged_attention(inp.q, inp.k_pool, inp.v_pool, inp.block_tables,
+                                            inp.seq_lens, scale, True)
+    e = max_err(o1, ref_o)
+    say(f"  max|dO|={e:.3e}")
+    assert e <= TOL_BF16 and lse_err(l1, ref_lse) <= TOL_LSE
+
+
 def test_paged_gqa_bit_identical_under_block_permutation(api):
     inp = _gqa_inputs((5, 100, 257, 1000), 2, 2, 4, seed=60)
     o1, l1 = _run_paged(api, inp, 3)
