@@ -79,15 +79,17 @@ long long checked_mul(std::initializer_list<long long> xs) {
 // towards enough (split, head, sequence) waves to cover the chip several times
 // as long as every split keeps at least 4 blocks. Grouped-query waves write
 // `group` partial rows per split and serve `group` heads from one read, so
-// they take splits of about 128 blocks and half the covering target; with
-// such long splits the kernel runs the longest sequences first, which evens
-// the end of the launch (64 sequences, 8 KV heads, group 8, 128 to 4096
-// keys: 2 splits longest-first 95 us, 4 splits in batch order 109 us).
+// they take splits of about 256 blocks and a quarter of the covering target:
+// such launches have few items, which then run four waves each (merged in
+// LDS), and with long splits the kernel runs the longest sequences first,
+// which evens the end of the launch (64 sequences, 8 KV heads, group 8, 128
+// to 4096 keys: 1 split 91.7 us, 2 splits 95-97 us, 4 splits in batch order
+// 109 us).
 int auto_splits(int B, int H, int max_blocks, int group) {
-  const long long per = group > 1 ? 128 : 32;
+  const long long per = group > 1 ? 256 : 32;
   long long s = ((long long)max_blocks + per - 1) / per;
   const long long waves = (long long)B * H;
-  long long fill = ((group > 1 ? 1024 : 2048) + waves - 1) / waves;
+  long long fill = ((group > 1 ? 512 : 2048) + waves - 1) / waves;
   if (fill > max_blocks / 4) fill = max_blocks / 4;
   if (s < fill) s = fill;
   if (s < 1) s = 1;
