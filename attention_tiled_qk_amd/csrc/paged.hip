@@ -167,7 +167,13 @@ void paged_attn_kernel(
 
   float m_run = -INFINITY;
   float mc_run = 0.f;  // cs * m_run, 0 while m_run is unset
-  float l_run = 0.f;
+  float l_run = 0.f;   // sum of the float32 P: the log-sum-exp
+  // bf16 cache: O is divided by the sum of the bf16 P that the PV products use,
+  // so the weights applied to V sum to one exactly (dot products of bf16 pairs
+  // with (1, 1)). The fp8 kernel folds the V scales into its P and divides by
+  // the float32 sum.
+  float l_used = 0.f;
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
   f32x4 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -336,6 +342,7 @@ void paged_attn_kernel(
       // an unchanged m (also -inf == -inf) keeps alpha = 1; m unset before gives 0
       const float alpha = m_new == m_run ? 1.f : exp2_fast((m_run - m_new) * cs);
       l_run *= alpha;
+      l_used *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       m_run = m_new;
@@ -356,6 +363,17 @@ void paged_attn_kernel(
     pw[2] = pack_bf16x2(e[4], e[5]);
     pw[3] = pack_bf16x2(e[6], e[7]);
     const bf16x8 p = __builtin_bit_cast(bf16x8, pw);
+    if constexpr (!F8) {
+      // the pairs as bf16x2 values of the bf16x8 (a pair bit-cast out of a
+      // just-written u32x4 element made this compiler keep only the first dot
+      // product and scale it by four)
+      const bf16x2* pp = reinterpret_cast<const bf16x2*>(&p);
+      const float d0 = __builtin_amdgcn_fdot2_f32_bf16(pp[0], ones, 0.f, false);
+      const float d1 = __builtin_amdgcn_fdot2_f32_bf16(pp[1], ones, d0, false);
+      const float d2 = __builtin_amdgcn_fdot2_f32_bf16(pp[2], ones, 0.f, false);
+      const float d3 = __builtin_amdgcn_fdot2_f32_bf16(pp[3], ones, d2, false);
+      l_used += d1 + d3;
+    }
 
     // V slabs -> LDS (row-major, padded rows), then transposing reads. The
     // workgroup is this one wave, whose LDS accesses execute in program order,
@@ -436,11 +454,13 @@ void paged_attn_kernel(
     // output columns and key positions) into wave 0, through LDS: waves 1 ..
     // WPS-1 leave (m, l, O) in their own staging areas
     static_assert(WPS == 2 || WPS == 4, "two or four waves per split");
+    static_assert((3 + 4 * DB) * 64 * sizeof(float) <= sizeof(vlds_raw[0]), "merge staging fits");
     __syncthreads();  // every wave is done with its LDS staging area
     if (wave != 0) {
-      float* xw = (float*)vlds_raw[wave];  // (2 + 4 DB) floats per lane
+      float* xw = (float*)vlds_raw[wave];  // (3 + 4 DB) floats per lane
       xw[lane] = m_run;
       xw[64 + lane] = l_run;
+      xw[128 + 4 * DB * 64 + lane] = l_used;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -454,6 +474,7 @@ void paged_attn_kernel(
     // an unchanged m (also -inf == -inf) keeps weight 1; an unset m gives 0
     const float a0 = m_run == m_new ? 1.f : exp2_fast((m_run - m_new) * cs);
     l_run *= a0;
+    l_used *= a0;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= a0;
 #pragma unroll
@@ -462,6 +483,7 @@ void paged_attn_kernel(
       const float mw = xw[lane];
       const float aw = mw == m_new ? 1.f : exp2_fast((mw - m_new) * cs);
       l_run += aw * xw[64 + lane];
+      l_used += aw * xw[128 + 4 * DB * 64 + lane];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -473,8 +495,13 @@ void paged_attn_kernel(
   // ---- epilogue
   float l_tot = sum_xor16(l_run);
   l_tot = sum_xor32(l_tot);
+  float l_norm = l_tot;
+  if constexpr (!F8) {
+    l_norm = sum_xor16(l_used);
+    l_norm = sum_xor32(l_norm);
+  }
   if (l16 < ncols) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_norm > 0.f ? 1.f / l_norm : 0.f;
     const float row_lse = l_tot > 0.f ? sc_abs * m_run + __logf(l_tot) : -INFINITY;
     if (num_splits == 1) {
       bf16* dst = o + qrow * D;
