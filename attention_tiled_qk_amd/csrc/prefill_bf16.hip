@@ -311,21 +311,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bool neg = scale < 0.f;
   const float sc_abs = neg ? -scale : scale;
   bf16x8 qreg[C::KC];
+  // Q: all loads issued together from a valid row (a row past L reads row 0
+  // and is zeroed after the load, by a select rather than a branch around the
+  // load: the branches let the compiler wait on the first loads before issuing
+  // the rest and the K/V tiles), then the first K/V tiles, then the sign flip
+  // and the zeroing, which wait for the Q data.
+  const bool q_ok = my_row < L;
+  u32x4 qraw[C::KC];
   {
-    const bool ok = my_row < L;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + qo_off + (ok ? my_row : 0) * row_stride + 8 * g);
-    const unsigned flip = neg ? 0x80008000u : 0u;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + qo_off + (q_ok ? my_row : 0) * row_stride + 8 * g);
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-      u32x4 w = ok ? src[kc * 2] : u32x4{0, 0, 0, 0};
-      w ^= flip;
-      qreg[kc] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int kc = 0; kc < C::KC; ++kc) qraw[kc] = src[kc * 2];
   }
 
   issue_k(std::integral_constant<int, 0>{}, 0);
   issue_v(std::integral_constant<int, 0>{}, 0);
   if (n_kt > 1) issue_k(std::integral_constant<int, 1>{}, 1);
+  {
+    const unsigned flip = neg ? 0x80008000u : 0u;
+    const unsigned keep = q_ok ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) qreg[kc] = __builtin_bit_cast(bf16x8, (qraw[kc] & keep) ^ flip);
+  }
 
   float m_run = -INFINITY;  // reference max (raw-score units)
   float mc_run = 0.f;       // c * m_run, 0 while m_run is unset
