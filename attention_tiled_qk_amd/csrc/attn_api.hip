@@ -74,19 +74,23 @@ long long checked_mul(std::initializer_list<long long> xs) {
 }
 
 // Split count for paged decode when the caller leaves it to the library:
-// splits of about 32 blocks (512 tokens) on the longest possible sequence, so
-// that waves carry similar amounts of work whatever the length mix, raised
-// towards enough (split, head, sequence) waves to cover the chip several times
-// as long as every split keeps at least 4 blocks. Grouped-query waves write
-// `group` partial rows per split and serve `group` heads from one read, so
-// they take splits of about 256 blocks and a quarter of the covering target:
-// such launches have few items, which then run four waves each (merged in
-// LDS), and with long splits the kernel runs the longest sequences first,
-// which evens the end of the launch (64 sequences, 8 KV heads, group 8, 128
-// to 4096 keys: 1 split 91.7 us, 2 splits 95-97 us, 4 splits in batch order
-// 109 us).
+// splits of about `per` blocks on the longest possible sequence, raised
+// towards enough (split, head, sequence) items to cover the chip several times
+// as long as every split keeps at least 4 blocks.
+// * Batches of up to 64 sequences run longest sequence first in the kernel,
+//   which evens the end of the launch when the splits are long; they take
+//   splits of about 128 blocks (64 sequences x 40 heads, 128 to 4096 keys: 2
+//   splits 413 us, 8 splits 430 us).
+// * Larger batches keep the batch order and splits of about 32 blocks (512
+//   tokens), so that items carry similar amounts of work whatever the length
+//   mix.
+// * Grouped-query items write `group` partial rows per split and serve `group`
+//   heads from one read; they take splits of about 256 blocks and a quarter of
+//   the covering target: such launches have few items, which then run four
+//   waves each (merged in LDS) (64 sequences, 8 KV heads, group 8: 1 split
+//   91.7 us, 2 splits 95-97 us, 4 splits in batch order 109 us).
 int auto_splits(int B, int H, int max_blocks, int group) {
-  const long long per = group > 1 ? 256 : 32;
+  const long long per = group > 1 ? 256 : B <= 64 ? 128 : 32;
   long long s = ((long long)max_blocks + per - 1) / per;
   const long long waves = (long long)B * H;
   long long fill = ((group > 1 ? 512 : 2048) + waves - 1) / waves;

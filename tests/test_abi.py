@@ -166,13 +166,22 @@ def test_workspace_bytes(api):
     assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 1) == 0
     assert L.attn_paged_workspace_bytes(0, 40, 5, 128, 2048, 16) == 0
     assert L.attn_paged_workspace_bytes(4, 40, 17, 128, 2048, 16) == 0
-    # automatic split count: about 32 blocks per split, raised towards 2048
-    # (split, head, sequence) waves while every split keeps >= 4 blocks
+    # automatic split count: about 128 blocks per split for batches of up to 64
+    # sequences (run longest first), 32 for larger ones, raised towards 2048
+    # (split, head, sequence) items while every split keeps >= 4 blocks
     assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 15, 0) == 4 * 3 * 129
     assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 3, 0) == 0
     assert L.attn_paged_workspace_bytes(1, 1, 1, 128, 256, 0) == 4 * 64 * 129
-    # the 64-sequence x 40-head decode shape with 256-block tables: 8 splits
-    assert L.attn_paged_workspace_bytes(64, 40, 1, 128, 256, 0) == 4 * 64 * 40 * 8 * 129
+    # the 64-sequence x 40-head decode shape with 256-block tables: 2 splits;
+    # one sequence more: 8 splits of 32 blocks
+    assert L.attn_paged_workspace_bytes(64, 40, 1, 128, 256, 0) == 4 * 64 * 40 * 2 * 129
+    assert L.attn_paged_workspace_bytes(65, 40, 1, 128, 256, 0) == 4 * 65 * 40 * 8 * 129
+    # long sequences, few of them: 2048-block tables, 4 x 40 heads -> 16 splits
+    assert L.attn_paged_workspace_bytes(4, 40, 5, 128, 2048, 0) == 4 * 4 * 40 * 5 * 16 * 129
+    # grouped-query heads (8 query heads per KV head): about 256 blocks per
+    # split, covering target 512 items: 64 x 8 KV heads of 256 blocks -> 1 split
+    assert L.attn_paged_gqa_workspace_bytes(64, 64, 8, 1, 128, 256, 0) == 0
+    assert L.attn_paged_gqa_workspace_bytes(4, 64, 8, 1, 128, 2048, 0) == 4 * 4 * 64 * 16 * 129
 
 
 def test_merge_and_gather_reject_bad_arguments(api):
