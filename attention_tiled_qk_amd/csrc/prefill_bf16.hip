@@ -253,7 +253,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const __amdgpu_buffer_rsrc_t k_pool_rs = buffer_rsrc(k, POOL ? pg.pool_bytes : 0);
   const __amdgpu_buffer_rsrc_t v_pool_rs = buffer_rsrc(v, POOL ? pg.pool_bytes : 0);
   const int lane_row = lane / C::NCH;
-  auto pool_off = [&](int kt, int i, i32x4 bl, unsigned lane_off) -> unsigned {
+  // `full`: the whole tile lies before the sequence's end (wave-uniform), so
+  // no lane needs the range check (all but the last tile of a sequence)
+  auto pool_off = [&](int kt, int i, i32x4 bl, unsigned lane_off, bool full) -> unsigned {
     const int off_in_tile = (wave + NW * i) * C::RPP;
     const int key = kt * BN + off_in_tile;
     const int which = off_in_tile >> 4;  // 0 .. 3, wave-uniform
@@ -261,13 +263,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int hi = (which & 1) ? bl[3] : bl[2];
     const unsigned id = (unsigned)__builtin_amdgcn_readfirstlane((which & 2) ? hi : lo);
     const unsigned base = ((id * (unsigned)pg.kv_heads + (unsigned)kvh) * 16u + (unsigned)(key & 15)) * (unsigned)C::ROWB;
+    if (full) return base + lane_off;
     return lane_row < Lk - key ? base + lane_off : 0x80000000u;
   };
   auto issue_k = [&](auto s, int kt) {
     if constexpr (PAGED && POOL) {
       const i32x4 bl = tile_blocks(kt);
+      if (kt * BN + BN <= Lk) {
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(k_pool_rs, kst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, koff));
+        for (int i = 0; i < C::PPW; ++i) dma16(k_pool_rs, kst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, koff, true));
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::PPW; ++i) dma16(k_pool_rs, kst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, koff, false));
+      }
     } else if constexpr (PAGED) {
       const i32x4 bl = tile_blocks(kt);
 #pragma unroll
@@ -281,8 +289,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto issue_v = [&](auto s, int kt) {
     if constexpr (PAGED && POOL) {
       const i32x4 bl = tile_blocks(kt);
+      if (kt * BN + BN <= Lk) {
 #pragma unroll
-      for (int i = 0; i < C::PPW; ++i) dma16(v_pool_rs, vst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, voff));
+        for (int i = 0; i < C::PPW; ++i) dma16(v_pool_rs, vst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, voff, true));
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::PPW; ++i) dma16(v_pool_rs, vst(s) + (wave + NW * i) * 1024, pool_off(kt, i, bl, voff, false));
+      }
     } else if constexpr (PAGED) {
       const i32x4 bl = tile_blocks(kt);
 #pragma unroll
